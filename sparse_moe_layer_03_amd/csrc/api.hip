@@ -1,0 +1,250 @@
+// C ABI of the MoE layer library: argument checks, workspace layout and the
+// launch sequence of each call.  Every check runs on the host before any
+// work is enqueued; no call allocates, frees or synchronises.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+static thread_local hipError_t g_last_hip = hipSuccess;
+
+int check_launch() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  static std::atomic<bool> init{false};
+  if (!init.load()) {
+    for (auto& c : cache) c.store(-1);
+    init.store(true);
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EHIP;
+  int n = cache[dev].load();
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return MOE_EHIP;
+  cache[dev].store(n);
+  return n;
+}
+
+static int elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+static int check_shape(const moe_shape* s) {
+  if (s == nullptr) return MOE_EINVAL;
+  if (s->T < 1 || s->n_ffn < 1 || s->n_zero < 0 || s->top_k < 1 || s->d_model < 1 || s->d_ff < 1)
+    return MOE_EINVAL;
+  const long E = (long)s->n_ffn + s->n_zero;
+  if (s->top_k > E) return MOE_EINVAL;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (E > 1024 || s->top_k > 16) return MOE_EUNSUPPORTED;
+  if (s->d_model % 64 != 0 || s->d_ff % 64 != 0) return MOE_EUNSUPPORTED;
+  if ((long)s->T * s->top_k >= (1L << 31)) return MOE_EUNSUPPORTED;
+  if (!isfinite(s->routed_scaling)) return MOE_ENONFINITE;
+  return MOE_OK;
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+struct WsLayout {
+  size_t logits, hist, h, total;
+};
+
+static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static WsLayout ws_layout(const moe_shape* s) {
+  const size_t E = (size_t)s->n_ffn + s->n_zero;
+  const size_t Tk = (size_t)s->T * s->top_k;
+  WsLayout w;
+  size_t off = 0;
+  w.logits = off;
+  off = up256(off + (size_t)s->T * E * sizeof(float));
+  w.hist = off;
+  off = up256(off + E * (size_t)dispatch_blocks((long)Tk) * sizeof(int32_t));
+  w.h = off;
+  off = up256(off + Tk * (size_t)s->d_ff * elem_size(s->dtype));
+  w.total = off;
+  return w;
+}
+
+// Few rows per expert -> 16-row tiles; otherwise 128x128 tiles.
+static int ffn_big_tiles(const moe_shape* s) {
+  const long E = (long)s->n_ffn + s->n_zero;
+  return ((long)s->T * s->top_k) / E >= 32;
+}
+
+static int router_big_tiles(const moe_shape* s, int cus) {
+  const long E = (long)s->n_ffn + s->n_zero;
+  const long tiles = ((long)s->T / 128) * ((E + 127) / 128);
+  return tiles >= cus;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return ws_layout(s).total;
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer or size out of range)";
+    case MOE_EUNSUPPORTED: return "shape or dtype outside the supported limits";
+    case MOE_EHIP: return hipGetErrorString(g_last_hip);
+    case MOE_ENONFINITE: return "non-finite parameter";
+    case MOE_EALIGN: return "pointer not aligned (16 bytes for bulk arrays, 4 for others)";
+    default: return "unknown status";
+  }
+}
+
+int moe_device_cu_count(void) { return device_cu_count(); }
+
+int moe_route(const moe_shape* s, const void* x, const void* w_router, const float* logit_bias,
+              const float* bias, int32_t* topk_idx, float* topk_gate, float* logits_out, void* ws,
+              void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!x || !w_router || !bias || !topk_idx || !topk_gate || (!logits_out && !ws)) return MOE_EINVAL;
+  if (!al16(x) || !al16(w_router) || (ws && !al16(ws)) || !al4(bias) || !al4(topk_idx) ||
+      !al4(topk_gate) || (logit_bias && !al4(logit_bias)) || (logits_out && !al4(logits_out)))
+    return MOE_EALIGN;
+  const int cus = device_cu_count();
+  if (cus <= 0) return MOE_EHIP;
+  hipStream_t st = (hipStream_t)stream;
+  const int E = s->n_ffn + s->n_zero;
+  float* logits = logits_out ? logits_out : (float*)((char*)ws + ws_layout(s).logits);
+  GemmArgs g{};
+  g.a = x;
+  g.b0 = w_router;
+  g.c = logits;
+  g.col_bias = logit_bias;
+  g.M = s->T;
+  g.N = E;
+  g.K = s->d_model;
+  g.ngroups = 1;
+  g.top_k = s->top_k;
+  rc = launch_gemm(s->dtype, 0, router_big_tiles(s, cus), g, st);
+  if (rc) return rc;
+  return launch_topk(logits, bias, s->T, E, s->top_k, s->routed_scaling, topk_idx, topk_gate, st);
+}
+
+int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm, void* ws,
+                 void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!topk_idx || !counts || !offsets || !perm || !inv_perm || !ws || (x_perm && !x))
+    return MOE_EINVAL;
+  if (!al4(topk_idx) || !al4(counts) || !al4(offsets) || !al4(perm) || !al4(inv_perm) ||
+      !al16(ws) || (x_perm && (!al16(x) || !al16(x_perm))))
+    return MOE_EALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const int E = s->n_ffn + s->n_zero;
+  const int Tk = s->T * s->top_k;
+  const int nb = dispatch_blocks(Tk);
+  int32_t* hist = (int32_t*)((char*)ws + ws_layout(s).hist);
+  rc = launch_dispatch(topk_idx, Tk, E, nb, hist, counts, offsets, perm, inv_perm, st);
+  if (rc) return rc;
+  if (x_perm)
+    rc = launch_gather(s->dtype, x, perm, offsets, s->n_ffn, Tk, s->top_k, s->d_model, x_perm, st);
+  return rc;
+}
+
+int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const int32_t* perm,
+                    const int32_t* offsets, const void* w_gate, const void* w_up, void* ws,
+                    void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!offsets || !w_gate || !w_up || !ws || (!x_perm && (!x || !perm))) return MOE_EINVAL;
+  if (!al4(offsets) || !al16(w_gate) || !al16(w_up) || !al16(ws) || (x_perm && !al16(x_perm)) ||
+      (!x_perm && (!al16(x) || !al4(perm))))
+    return MOE_EALIGN;
+  GemmArgs g{};
+  g.a = x_perm ? x_perm : x;
+  g.perm = x_perm ? nullptr : perm;
+  g.offsets = offsets;
+  g.b0 = w_gate;
+  g.b1 = w_up;
+  g.c = (char*)ws + ws_layout(s).h;
+  g.N = s->d_ff;
+  g.K = s->d_model;
+  g.M = s->T;
+  g.ngroups = s->n_ffn;
+  g.top_k = s->top_k;
+  return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
+}
+
+int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down, void* y_perm,
+                 void* ws, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!offsets || !w_down || !y_perm || !ws) return MOE_EINVAL;
+  if (!al4(offsets) || !al16(w_down) || !al16(y_perm) || !al16(ws)) return MOE_EALIGN;
+  GemmArgs g{};
+  g.a = (char*)ws + ws_layout(s).h;
+  g.offsets = offsets;
+  g.b0 = w_down;
+  g.c = y_perm;
+  g.N = s->d_model;
+  g.K = s->d_ff;
+  g.ngroups = s->n_ffn;
+  g.top_k = s->top_k;
+  return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);
+}
+
+int moe_expert_ffn(const moe_shape* s, const void* x, const void* x_perm, const int32_t* perm,
+                   const int32_t* offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, void* y_perm, void* ws, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!w_down || !y_perm) return MOE_EINVAL;
+  if (!al16(w_down) || !al16(y_perm)) return MOE_EALIGN;
+  rc = moe_ffn_gate_up(s, x, x_perm, perm, offsets, w_gate, w_up, ws, stream);
+  if (rc) return rc;
+  return moe_ffn_down(s, offsets, w_down, y_perm, ws, stream);
+}
+
+int moe_combine(const moe_shape* s, const void* x, const void* y_perm, const int32_t* topk_idx,
+                const float* topk_gate, const int32_t* inv_perm, void* y, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!x || !y_perm || !topk_idx || !topk_gate || !inv_perm || !y) return MOE_EINVAL;
+  if (!al16(x) || !al16(y_perm) || !al16(y) || !al4(topk_idx) || !al4(topk_gate) ||
+      !al4(inv_perm))
+    return MOE_EALIGN;
+  return launch_combine(s->dtype, x, y_perm, topk_idx, topk_gate, inv_perm, s->T, s->d_model,
+                        s->top_k, s->n_ffn, y, (hipStream_t)stream);
+}
+
+int moe_pid_update(const moe_shape* s, const moe_pid_params* pp, const int32_t* counts,
+                   moe_pid_state* state, float* bias, float* r_log, int32_t r_log_len,
+                   void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!pp || !counts || !state || !bias || (r_log && r_log_len < 0)) return MOE_EINVAL;
+  if (!isfinite(pp->setpoint) || !isfinite(pp->kp) || !isfinite(pp->ki) || !isfinite(pp->kd))
+    return MOE_ENONFINITE;
+  if (!al4(counts) || !al4(state) || !al4(bias) || (r_log && !al4(r_log))) return MOE_EALIGN;
+  return launch_pid(counts, s->n_ffn, s->T, pp->setpoint, pp->kp, pp->ki, pp->kd, state, bias,
+                    r_log, r_log ? r_log_len : 0, (hipStream_t)stream);
+}
+
+}  // extern "C"

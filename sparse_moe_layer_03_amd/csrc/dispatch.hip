@@ -1,0 +1,172 @@
+// Dispatch: per-expert histogram, exclusive prefix sum and a stable
+// permutation of the T*k assignments (LongCat-2.0 Ascend deployment
+// article, section "底层定制算子深度优化": Dispatch with zero-computation
+// experts).  Deterministic: LDS atomics only count (integer adds commute);
+// every rank is derived from assignment order, never from atomic order.
+//
+//   hist    nb blocks: block b counts its contiguous chunk of assignments
+//           into LDS and writes the expert-major table hist[e * nb + b].
+//   scan    one block: exclusive scan of that table -> the first sorted
+//           position of (expert e, chunk b); counts and offsets.
+//   scatter nb blocks: each of the 4 waves of block b owns a quarter of the
+//           chunk; wave-level histograms give each wave its starting
+//           position per expert, then the wave walks its quarter 64
+//           assignments at a time, ranking equal experts among the lanes
+//           with a ballot-built peer mask.
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+constexpr int kDispThreads = 256;
+
+__global__ void __launch_bounds__(kDispThreads)
+dispatch_hist_kernel(const int32_t* __restrict__ idx, int Tk, int E, int32_t* __restrict__ hist) {
+  extern __shared__ int s_h[];
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int chunk = (Tk + nb - 1) / nb;
+  const int lo = b * chunk, hi = min(Tk, lo + chunk);
+  for (int e = threadIdx.x; e < E; e += kDispThreads) s_h[e] = 0;
+  __syncthreads();
+  for (int a = lo + threadIdx.x; a < hi; a += kDispThreads) {
+    const int e = idx[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_h[e], 1);  // ids are in range by contract
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kDispThreads) hist[(size_t)e * nb + b] = s_h[e];
+}
+
+// Single block of 1024 threads; each thread scans a contiguous segment.
+__global__ void __launch_bounds__(1024)
+dispatch_scan_kernel(int32_t* __restrict__ hist, int nb, int E, int Tk,
+                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  __shared__ int s_tmp[1024 / 64];
+  const int n = E * nb;
+  const int per = (n + 1023) / 1024;
+  const int lo = threadIdx.x * per, hi = min(n, lo + per);
+  int sum = 0;
+  for (int i = lo; i < hi; ++i) sum += hist[i];
+  // counts per expert (independent of the scan)
+  const int incl = block_inclusive_scan<1024>(sum, s_tmp);
+  int run = incl - sum;
+  for (int i = lo; i < hi; ++i) {
+    const int v = hist[i];
+    hist[i] = run;  // becomes the start position of (e, b)
+    run += v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const int start = hist[(size_t)e * nb];
+    const int end = (e + 1 < E) ? hist[(size_t)(e + 1) * nb] : Tk;
+    offsets[e] = start;
+    counts[e] = end - start;
+  }
+  if (threadIdx.x == 0) offsets[E] = Tk;
+}
+
+template <int NBITS>
+__global__ void __launch_bounds__(kDispThreads)
+dispatch_scatter_kernel(const int32_t* __restrict__ idx, int Tk, int E,
+                        const int32_t* __restrict__ base, int32_t* __restrict__ perm,
+                        int32_t* __restrict__ inv_perm) {
+  extern __shared__ int s_w[];  // [4][E]
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int chunk = (Tk + nb - 1) / nb;
+  const int lo = b * chunk, hi = min(Tk, lo + chunk);
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int sub = (chunk + 3) / 4;
+  const int wlo = min(hi, lo + w * sub), whi = min(hi, wlo + sub);
+
+  for (int i = threadIdx.x; i < 4 * E; i += kDispThreads) s_w[i] = 0;
+  __syncthreads();
+  for (int a = wlo + lane; a < whi; a += 64) {
+    const int e = idx[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_w[w * E + e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kDispThreads) {
+    int run = base[(size_t)e * nb + b];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = s_w[q * E + e];
+      s_w[q * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  int* my = s_w + w * E;
+  for (int a0 = wlo; a0 < whi; a0 += 64) {
+    const int a = a0 + lane;
+    const int e0 = (a < whi) ? idx[a] : -1;
+    const bool valid = (unsigned)e0 < (unsigned)E;
+    const int e = valid ? e0 : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < NBITS; ++bit) {
+      const bool s = (e >> bit) & 1;
+      const uint64_t m = __ballot(s);
+      peers &= s ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(peers & lanemask_lt());
+      const int pos = my[e] + rank;
+      perm[pos] = a;
+      inv_perm[a] = pos;
+    }
+    // the highest lane of each peer group advances that expert's cursor
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers >> lane) == 1ull) my[e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int launch_dispatch(const int32_t* idx, int Tk, int E, int nb, int32_t* block_hist,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                    hipStream_t st) {
+  hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nb), dim3(kDispThreads), E * sizeof(int), st,
+                     idx, Tk, E, block_hist);
+  int rc = check_launch();
+  if (rc) return rc;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, block_hist, nb, E, Tk,
+                     counts, offsets);
+  rc = check_launch();
+  if (rc) return rc;
+  const size_t lds = 4 * (size_t)E * sizeof(int);
+  if (E <= 256)
+    hipLaunchKernelGGL(dispatch_scatter_kernel<8>, dim3(nb), dim3(kDispThreads), lds, st, idx, Tk,
+                       E, block_hist, perm, inv_perm);
+  else
+    hipLaunchKernelGGL(dispatch_scatter_kernel<10>, dim3(nb), dim3(kDispThreads), lds, st, idx,
+                       Tk, E, block_hist, perm, inv_perm);
+  return check_launch();
+}
+
+// x_perm[p] = x[perm[p] / k] for p < offsets[n_ffn]; one block per row.
+template <typename T>
+__global__ void __launch_bounds__(256)
+gather_rows_kernel(const T* __restrict__ x, const int32_t* __restrict__ perm,
+                   const int32_t* __restrict__ offsets, int n_ffn, int k, int d,
+                   T* __restrict__ x_perm) {
+  const int p = blockIdx.x;
+  if (p >= offsets[n_ffn]) return;
+  const int tok = perm[p] / k;
+  constexpr int CE = 16 / sizeof(T);
+  const char* src = (const char*)(x + (size_t)tok * d);
+  char* dst = (char*)(x_perm + (size_t)p * d);
+  for (int c = threadIdx.x; c < d / CE; c += 256) st16(dst + c * 16, ld16(src + c * 16));
+}
+
+int launch_gather(int dtype, const void* x, const int32_t* perm, const int32_t* offsets,
+                  int n_ffn, int Tk, int k, int d, void* x_perm, hipStream_t st) {
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(gather_rows_kernel<__bf16>, dim3(Tk), dim3(256), 0, st,
+                       (const __bf16*)x, perm, offsets, n_ffn, k, d, (__bf16*)x_perm);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<float>, dim3(Tk), dim3(256), 0, st, (const float*)x,
+                       perm, offsets, n_ffn, k, d, (float*)x_perm);
+  return check_launch();
+}
+
+}  // namespace moe

@@ -1,0 +1,303 @@
+// Grouped GEMM on gfx950 MFMA for the MoE layer: the router classifier, the
+// experts' gate/up projections with a fused SwiGLU epilogue, and the experts'
+// down projections.
+//
+// Every operand has its reduction dimension contiguous (x rows, H rows and
+// the out-major weights), so a 16-byte chunk of one row is exactly the
+// 8 bf16 (or 4 fp32) values one lane feeds to a 16x16 MFMA.  Tiles of A
+// (token rows) and B (weight rows) are staged in LDS as 128-byte rows per
+// K-step, with the chunk index XOR-swizzled by (row & 7) so that both the
+// row-wise global->LDS stores and the fragment reads are bank-conflict free.
+// Two LDS stages: the next K-step's global loads are in flight while the
+// current stage feeds the MFMAs.
+//
+// Work is a persistent loop over (group, n-tile, m-tile) tiles.  Each
+// workgroup derives the tile list itself from the group offsets, so no host
+// synchronisation is needed to learn how many rows each expert received.
+// Workgroup ids are remapped so that consecutive tiles land on the same XCD
+// (dispatch is round-robin over the 8 XCDs), which keeps an expert's weight
+// tile and its token rows in that XCD's L2 while its m-tiles run.
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+enum { MODE_ROUTER = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
+
+constexpr int kMaxGroups = 1024;
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+template <typename T> struct Mfma;
+template <> struct Mfma<__bf16> {
+  // one 16-byte chunk per lane = the whole K=32 slice of a 16x16x32 MFMA
+  static __device__ __forceinline__ f32x4_t step(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  // a 16-byte chunk holds 4 K values: four 16x16x4 fp32 MFMAs
+  static __device__ __forceinline__ f32x4_t step(u32x4_t a, u32x4_t b, f32x4_t c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[s]), __uint_as_float(b[s]), c, 0, 0, 0);
+    return c;
+  }
+};
+
+template <typename T, int MODE, int BM, int BN, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
+grouped_gemm_kernel(GemmArgs g) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int CE = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int BK = 8 * CE;                // elements per K-step (128 bytes)
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  constexpr int HN = (MODE == MODE_GATE_UP) ? BN / 2 : BN;  // output cols per tile
+  static_assert(MB >= 1 && NB >= 1, "wave tile too small");
+  static_assert(MODE != MODE_GATE_UP || NB % 2 == 0, "gate/up pairing");
+  constexpr int A_CH = BM * 8, B_CH = BN * 8;
+  constexpr int A_IT = (A_CH + NT - 1) / NT, B_IT = (B_CH + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) char s_a[2][BM * 128];
+  __shared__ __attribute__((aligned(16))) char s_b[2][BN * 128];
+  __shared__ int s_mt[kMaxGroups + 1];
+  __shared__ int s_tmp[NT / 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int r16 = lane & 15, kg = lane >> 4;
+
+  // ---- tile list: per-group m-tile prefix sums in LDS
+  const int ngroups = (MODE == MODE_ROUTER) ? 1 : g.ngroups;
+  {
+    constexpr int PER = (kMaxGroups + NT - 1) / NT;
+    int loc[PER];
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int gi = tid * PER + i;
+      int mt = 0;
+      if (gi < ngroups) {
+        const int cnt = (MODE == MODE_ROUTER) ? g.M : (g.offsets[gi + 1] - g.offsets[gi]);
+        mt = (cnt + BM - 1) / BM;
+      }
+      run += mt;
+      loc[i] = run;
+    }
+    const int incl = block_inclusive_scan<NT>(run, s_tmp);
+    const int base = incl - run;
+    if (tid == 0) s_mt[0] = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int gi = tid * PER + i;
+      if (gi < ngroups) s_mt[gi + 1] = base + loc[i];
+    }
+    __syncthreads();
+  }
+  const int ntiles = (g.N + HN - 1) / HN;
+  const long total = (long)s_mt[ngroups] * ntiles;
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int vid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int nK = g.K / BK;
+  const size_t a_row_bytes = (size_t)g.K * sizeof(T);
+
+  for (long t = vid; t < total; t += G) {
+    // locate group: last gi with s_mt[gi] * ntiles <= t
+    int lo = 0, hi = ngroups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long)s_mt[mid] * ntiles <= t) lo = mid; else hi = mid - 1;
+    }
+    const int grp = lo;
+    const int mt_g = s_mt[grp + 1] - s_mt[grp];
+    const long local = t - (long)s_mt[grp] * ntiles;
+    const int nt = (int)(local / mt_g), mi = (int)(local % mt_g);
+    const int row0 = (MODE == MODE_ROUTER) ? 0 : g.offsets[grp];
+    const int rows = (MODE == MODE_ROUTER) ? g.M : (g.offsets[grp + 1] - row0);
+    const int m0 = mi * BM;
+    const int n0 = nt * HN;
+
+    // ---- per-thread source pointers for this tile
+    const char* a_src[A_IT];
+    const char* b_src[B_IT];
+    int a_lds[A_IT], b_lds[B_IT];
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it) {
+      const int q = tid + it * NT;
+      const int r = q >> 3, c = q & 7;
+      int rr = m0 + r;
+      if (rr > rows - 1) rr = rows - 1;  // ragged tail: reload a valid row
+      long src_row;
+      if (q >= A_CH)
+        src_row = row0;
+      else if (MODE == MODE_GATE_UP && g.perm != nullptr)
+      {
+        src_row = g.perm[row0 + rr] / g.top_k;  // gather token rows on load
+        if (src_row < 0 || src_row >= g.M) src_row = 0;
+      }
+      else
+        src_row = row0 + rr;
+      a_src[it] = (q < A_CH) ? (const char*)g.a + src_row * a_row_bytes + c * 16 : nullptr;
+      a_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
+    }
+#pragma unroll
+    for (int it = 0; it < B_IT; ++it) {
+      const int q = tid + it * NT;
+      const int r = q >> 3, c = q & 7;
+      const char* base;
+      int n;
+      if (MODE == MODE_GATE_UP) {
+        const bool up = r >= HN;
+        n = n0 + (up ? r - HN : r);
+        if (n > g.N - 1) n = g.N - 1;
+        base = (const char*)(up ? g.b1 : g.b0) + (size_t)grp * g.N * a_row_bytes;
+      } else {
+        n = n0 + r;
+        if (n > g.N - 1) n = g.N - 1;
+        base = (const char*)g.b0 + (MODE == MODE_DOWN ? (size_t)grp * g.N * a_row_bytes : 0);
+      }
+      b_src[it] = (q < B_CH) ? base + (size_t)n * a_row_bytes + c * 16 : nullptr;
+      b_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
+    }
+
+    f32x4_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t ra[A_IT], rb[B_IT];
+    auto gload = [&](int ks) {
+      const size_t off = (size_t)ks * 128;
+#pragma unroll
+      for (int it = 0; it < A_IT; ++it)
+        if (tid + it * NT < A_CH) ra[it] = ld16(a_src[it] + off);
+#pragma unroll
+      for (int it = 0; it < B_IT; ++it)
+        if (tid + it * NT < B_CH) rb[it] = ld16(b_src[it] + off);
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int it = 0; it < A_IT; ++it)
+        if (tid + it * NT < A_CH) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_lds[it]]) = ra[it];
+#pragma unroll
+      for (int it = 0; it < B_IT; ++it)
+        if (tid + it * NT < B_CH) *reinterpret_cast<u32x4_t*>(&s_b[buf][b_lds[it]]) = rb[it];
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int ks = 0; ks < nK; ++ks) {
+      const int buf = ks & 1;
+      if (ks + 1 < nK) gload(ks + 1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int c = kk * 4 + kg;
+        u32x4_t af[MB], bfr[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int r = wm * WTM + i * 16 + r16;
+          af[i] = *reinterpret_cast<const u32x4_t*>(&s_a[buf][r * 128 + ((c ^ (r & 7)) << 4)]);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          int r;
+          if (MODE == MODE_GATE_UP)
+            r = (j < NB / 2) ? wn * (WTN / 2) + j * 16 + r16
+                             : HN + wn * (WTN / 2) + (j - NB / 2) * 16 + r16;
+          else
+            r = wn * WTN + j * 16 + r16;
+          bfr[j] = *reinterpret_cast<const u32x4_t*>(&s_b[buf][r * 128 + ((c ^ (r & 7)) << 4)]);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::step(af[i], bfr[j], acc[i][j]);
+      }
+      if (ks + 1 < nK) lstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue: lane holds C[4*kg + v][r16] of each 16x16 block
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = m0 + wm * WTM + i * 16 + 4 * kg + v;
+        if (r >= rows) continue;
+        if (MODE == MODE_GATE_UP) {
+#pragma unroll
+          for (int j = 0; j < NB / 2; ++j) {
+            const int col = n0 + wn * (WTN / 2) + j * 16 + r16;
+            if (col < g.N) {
+              const float h = silu_f(acc[i][j][v]) * acc[i][j + NB / 2][v];
+              ((T*)g.c)[(size_t)(row0 + r) * g.N + col] = ElemOps<T>::from_f(h);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int col = n0 + wn * WTN + j * 16 + r16;
+            if (col < g.N) {
+              if (MODE == MODE_ROUTER)
+                ((float*)g.c)[(size_t)r * g.N + col] =
+                    acc[i][j][v] + (g.col_bias != nullptr ? g.col_bias[col] : 0.f);
+              else
+                ((T*)g.c)[(size_t)(row0 + r) * g.N + col] = ElemOps<T>::from_f(acc[i][j][v]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch --
+
+template <typename T, int MODE, int BM, int BN, int WM, int WN>
+static int launch_cfg(const GemmArgs& g, hipStream_t st) {
+  auto kern = grouped_gemm_kernel<T, MODE, BM, BN, WM, WN>;
+  constexpr int NT = 64 * WM * WN;
+  static int per_cu = -1;  // occupancy of this instantiation (device-independent here)
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, 0) != hipSuccess || n < 1) n = 1;
+    per_cu = n;
+  }
+  const int cus = device_cu_count();
+  if (cus <= 0) return MOE_EHIP;
+  int grid = cus * per_cu;
+  grid -= grid % 8;
+  if (grid < 8) grid = 8;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, g);
+  return check_launch();
+}
+
+template <typename T>
+static int launch_typed(int mode, int big, const GemmArgs& g, hipStream_t st) {
+  if (big) {
+    switch (mode) {
+      case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, 128, 128, 2, 2>(g, st);
+      case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, 128, 128, 2, 2>(g, st);
+      default: return launch_cfg<T, MODE_DOWN, 128, 128, 2, 2>(g, st);
+    }
+  }
+  switch (mode) {
+    case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, 16, 128, 1, 4>(g, st);
+    case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, 16, 128, 1, 4>(g, st);
+    default: return launch_cfg<T, MODE_DOWN, 16, 128, 1, 4>(g, st);
+  }
+}
+
+int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st) {
+  if (dtype == MOE_BF16) return launch_typed<__bf16>(mode, big, g, st);
+  return launch_typed<float>(mode, big, g, st);
+}
+
+}  // namespace moe

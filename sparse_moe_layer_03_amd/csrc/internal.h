@@ -1,0 +1,59 @@
+// Internal host-side interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+struct GemmArgs {
+  const void* a;           // token rows: x (router, gate/up) or H (down)
+  const int32_t* perm;     // gate/up: gather rows x[perm[p] / top_k]; else null
+  const int32_t* offsets;  // group row offsets [ngroups + 1] (gate/up, down)
+  const void* b0;          // W_router | W_gate | W_down
+  const void* b1;          // W_up (gate/up only)
+  void* c;                 // logits fp32 [M, N] | H [rows, N] | y_perm [rows, N]
+  const float* col_bias;   // router: per-column logit offset [N] or null
+  int M;                   // router: T (grouped modes use offsets)
+  int N;                   // output columns: E | d_ff | d_model
+  int K;                   // reduction length: d_model | d_model | d_ff
+  int ngroups;             // experts (grouped modes)
+  int top_k;
+};
+
+// mode: 0 router, 1 gate/up + SwiGLU, 2 down.  big: 128x128 tiles, else
+// 16-row tiles for few rows per expert.
+int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st);
+
+int launch_topk(const float* logits, const float* bias, int T, int E, int k,
+                float scaling, int32_t* idx, float* gate, hipStream_t st);
+
+int launch_dispatch(const int32_t* idx, int Tk, int E, int nb, int32_t* block_hist,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                    hipStream_t st);
+
+int launch_gather(int dtype, const void* x, const int32_t* perm, const int32_t* offsets,
+                  int n_ffn, int Tk, int k, int d, void* x_perm, hipStream_t st);
+
+int launch_combine(int dtype, const void* x, const void* y_perm, const int32_t* idx,
+                   const float* gate, const int32_t* inv_perm, int T, int d, int k,
+                   int n_ffn, void* y, hipStream_t st);
+
+int launch_pid(const int32_t* counts, int n_ffn, int T, float setpoint, float kp, float ki,
+               float kd, moe_pid_state* state, float* bias, float* r_log, int r_log_len,
+               hipStream_t st);
+
+int device_cu_count();
+int check_launch();
+
+// Number of blocks the dispatch kernels split T*k assignments into.
+inline int dispatch_blocks(long Tk) {
+  long nb = (Tk + 1023) / 1024;
+  if (nb < 1) nb = 1;
+  if (nb > 256) nb = 256;
+  return (int)nb;
+}
+
+}  // namespace moe

@@ -1,0 +1,56 @@
+// PID step on the router bias, one wave64 (snilld.dk LongCat-2.0 article,
+// section "MoE i praksis og prisen for fleksibilitet": a PID controller
+// adjusts the router bias so that activation stays in the desired range).
+//
+// Measured value: r = FFN assignments / T, the mean number of real experts
+// per token.  Incremental form: every FFN expert's bias moves by
+//   delta = (kp*err + ki*I) + kd*D,   err = setpoint - r,  I += err,
+//   D = err - prev_err (0 on the first step).
+// Every product and sum is rounded separately (no contraction into FMA), in
+// this order.  The count sum is an integer reduction, so r is exact up to
+// one division.
+
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+__global__ void __launch_bounds__(64)
+pid_kernel(const int32_t* __restrict__ counts, int n_ffn, int T, float setpoint, float kp,
+           float ki, float kd, moe_pid_state* __restrict__ state, float* __restrict__ bias,
+           float* __restrict__ r_log, int r_log_len) {
+  const int lane = threadIdx.x;
+  int a = 0;
+  for (int e = lane; e < n_ffn; e += 64) a += counts[e];
+  a = wave_sum_i(a);
+  const float integral = state->integral, prev = state->prev_err;
+  const int step = state->step;
+  if (!isfinite(integral) || !isfinite(prev)) {
+    if (lane == 0) state->flags |= 1;
+    return;
+  }
+  const float r = __fdiv_rn((float)a, (float)T);
+  const float err = __fsub_rn(setpoint, r);
+  const float I = __fadd_rn(integral, err);
+  const float D = (step == 0) ? 0.f : __fsub_rn(err, prev);
+  const float delta = __fadd_rn(__fadd_rn(__fmul_rn(kp, err), __fmul_rn(ki, I)), __fmul_rn(kd, D));
+  for (int e = lane; e < n_ffn; e += 64) bias[e] = __fadd_rn(bias[e], delta);
+  if (lane == 0) {
+    if (r_log != nullptr && step >= 0 && step < r_log_len) r_log[step] = r;
+    state->integral = I;
+    state->prev_err = err;
+    state->step = step + 1;
+  }
+}
+
+int launch_pid(const int32_t* counts, int n_ffn, int T, float setpoint, float kp, float ki,
+               float kd, moe_pid_state* state, float* bias, float* r_log, int r_log_len,
+               hipStream_t st) {
+  hipLaunchKernelGGL(pid_kernel, dim3(1), dim3(64), 0, st, counts, n_ffn, T, setpoint, kp, ki,
+                     kd, state, bias, r_log, r_log_len);
+  return check_launch();
+}
+
+}  // namespace moe

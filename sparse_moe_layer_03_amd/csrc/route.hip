@@ -1,0 +1,120 @@
+// Softmax + biased top-k + gates, one wave64 per token.
+//
+// LongCat-2.0 data sheet (archdb), table "Mixture of experts": the router
+// scores FFN and identity experts together and selects the top k by score
+// plus e_score_correction_bias; the gates are the unbiased scores times the
+// routed scaling factor, not renormalised.
+//
+// Each lane holds experts lane, lane+64, ... in registers (E <= 1024 -> at
+// most 16 per lane).  The softmax max/sum and every selection round are
+// butterfly reductions over the wave in a fixed order, so the result is
+// deterministic.  Selection compares (key, -id): larger key wins, equal keys
+// go to the lower expert id.  The chosen set is emitted in ascending expert
+// id with a ballot per register slot.
+
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+
+template <int PL>
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
+            int k, float scaling, int32_t* __restrict__ idx, float* __restrict__ gate) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform per wave
+  const float* row = logits + (size_t)t * E;
+
+  float l[PL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + 64 * i;
+    l[i] = (e < E) ? row[e] : -INFINITY;
+    m = fmaxf(m, l[i]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+  float p[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = (e < E) ? expf(l[i] - m) : 0.f;
+    s += p[i];
+  }
+  s = wave_sum(s);
+  float key[PL];
+  bool avail[PL], sel[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = p[i] / s;
+    avail[i] = e < E;
+    sel[i] = false;
+    key[i] = avail[i] ? p[i] + bias[e] : 0.f;
+    if (key[i] != key[i]) key[i] = -INFINITY;  // NaN never outranks a number
+  }
+
+  for (int r = 0; r < k; ++r) {
+    float bk = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      if (avail[i] && (key[i] > bk || (key[i] == bk && e < bid))) {
+        bk = key[i];
+        bid = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, kWave);
+      const int oid = __shfl_xor(bid, o, kWave);
+      if (ok > bk || (ok == bk && oid < bid)) {
+        bk = ok;
+        bid = oid;
+      }
+    }
+    if ((bid & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (i == (bid >> 6)) {
+          avail[i] = false;
+          sel[i] = true;
+        }
+    }
+  }
+
+  int pos = 0;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const uint64_t bal = __ballot(sel[i]);
+    if (sel[i]) {
+      const int o = t * k + pos + __popcll(bal & lanemask_lt());
+      idx[o] = lane + 64 * i;
+      gate[o] = scaling * p[i];
+    }
+    pos += __popcll(bal);
+  }
+}
+
+int launch_topk(const float* logits, const float* bias, int T, int E, int k, float scaling,
+                int32_t* idx, float* gate, hipStream_t st) {
+  const dim3 grid((T + 3) / 4), block(256);
+  if (E <= 64)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+  else if (E <= 128)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+  else if (E <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+  else if (E <= 512)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+  else
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+  return check_launch();
+}
+
+}  // namespace moe

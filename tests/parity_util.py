@@ -1,0 +1,167 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the oracle under the routing certification rule.
+
+Routing rule.  Several selected sets are correct when two keys sit within
+rounding distance of the top-k boundary.  A token is *certified* when the
+oracle's gap between its k-th and (k+1)-th key exceeds a bound on how far
+the GPU's fp32 key can lie from the oracle's; certified tokens must match
+the oracle's set exactly, the others must be a valid top-k of the oracle's
+keys within that bound.  Integer arrays (counts, offsets, perm, inv_perm)
+must then equal the oracle's counting sort of the GPU's own selection
+exactly, and the layer output is compared with the oracle evaluated on the
+GPU's selection, with the oracle's own gates.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+from sparse_moe_layer_03_amd import binding as B
+from sparse_moe_layer_03_amd import synth as S
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def row_rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    den = np.where(den == 0, 1.0, den)
+    return num / den
+
+
+class Model:
+    """Device weights of one layer (synthetic, seeded)."""
+
+    def __init__(self, w: S.Workload, device="cuda", zipf_alpha=None, bias=None):
+        self.w = w
+        self.dt = S.torch_dtype(w.dtype)
+        self.wr = S.make_router(w, device)
+        self.bias = (S.make_bias(w, device) if bias is None
+                     else torch.as_tensor(bias, dtype=torch.float32, device=device))
+        self.lb = None
+        if w.zipf_s:
+            self.lb = S.zipf_logit_offset(w, zipf_alpha, device)
+        self.wg, self.wu, self.wd = S.make_experts(w, device)
+        self.shape = B.make_shape(w.T, w.d_model, w.n_ffn, w.n_zero, w.d_ff, w.top_k, w.dtype,
+                                  w.routed_scaling)
+
+
+def run_gpu(m: Model, x, buf=None, with_logits=True, x_perm=False):
+    s = m.shape
+    if buf is None:
+        buf = B.LayerBuffers(s, x.device, x_perm=x_perm)
+    logits = (torch.empty((s.T, s.n_ffn + s.n_zero), dtype=torch.float32, device=x.device)
+              if with_logits else None)
+    B.layer_forward(buf, x, m.wr, m.bias, m.wg, m.wu, m.wd, logit_bias=m.lb, logits_out=logits)
+    torch.cuda.synchronize()
+    out = dict(topk_idx=buf.topk_idx.cpu().numpy(), topk_gate=buf.topk_gate.cpu().numpy(),
+               counts=buf.counts.cpu().numpy(), offsets=buf.offsets.cpu().numpy(),
+               perm=buf.perm.cpu().numpy(), inv_perm=buf.inv_perm.cpu().numpy(),
+               y=S.to_numpy64(buf.y))
+    if logits is not None:
+        out["logits"] = logits.cpu().numpy().astype(np.float64)
+    return out, buf
+
+
+def check_routing(gpu, ref, k, logit_tol, report=None):
+    """Compare GPU routing with the oracle's route() output (fp64 scores)."""
+    T = gpu["topk_idx"].shape[0]
+    dl = np.abs(gpu["logits"] - ref["logits"]).max()
+    assert dl <= logit_tol, f"router logits differ by {dl} > {logit_tol}"
+    p = ref["p"]
+    keys = ref["keys"].astype(np.float64)
+    # bound on |key_gpu - key_oracle|: score error from the logit error plus
+    # fp32 rounding of the score and of the sum with the bias
+    eps = max(dl, 1e-7)
+    delta = 4.0 * eps * p.max(axis=1) + 4.0 * np.abs(keys).max(axis=1) * 2.0 ** -24
+    margin = O.topk_margin(keys, k)
+    cert = margin > 2.0 * delta
+    g_idx = gpu["topk_idx"]
+    assert (np.diff(g_idx, axis=1) > 0).all(), "GPU sets not in ascending expert id"
+    bad = np.nonzero(cert & (g_idx != ref["topk_idx"]).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} certified tokens differ, e.g. token {bad[:5]}"
+    n_unc = int((~cert).sum())
+    for t in np.nonzero(~cert)[0]:
+        sel = np.zeros(keys.shape[1], bool)
+        sel[g_idx[t]] = True
+        assert keys[t, sel].min() >= keys[t, ~sel].max() - 2.0 * delta[t], f"token {t} invalid"
+    if report is not None:
+        report["uncertified"] = n_unc
+        report["logit_maxdiff"] = float(dl)
+    return n_unc
+
+
+def check_gates(gpu, ref, scaling, rtol):
+    exp_g = scaling * np.take_along_axis(ref["p"], gpu["topk_idx"].astype(np.int64), axis=1)
+    np.testing.assert_allclose(gpu["topk_gate"], exp_g, rtol=rtol, atol=1e-9)
+
+
+def check_dispatch(gpu, E):
+    d = O.dispatch(gpu["topk_idx"], E)
+    for key in ("counts", "offsets", "perm", "inv_perm"):
+        np.testing.assert_array_equal(gpu[key], d[key], err_msg=key)
+    return d
+
+
+def oracle_outputs_for_tokens(m: Model, x_dev, tokens, gpu_idx):
+    """Oracle layer output for a subset of tokens, on the GPU's selection,
+    streaming one touched expert's weights to the host at a time."""
+    w = m.w
+    tokens = np.asarray(tokens)
+    xs = S.to_numpy64(x_dev[torch.as_tensor(tokens, device=x_dev.device)])
+    wr = S.to_numpy64(m.wr)
+    lb = None if m.lb is None else m.lb.cpu().numpy().astype(np.float64)
+    r = O.route(xs, wr, m.bias.cpu().numpy(), w.top_k, w.routed_scaling, lb)
+    idx = gpu_idx[tokens]
+    gate = w.routed_scaling * np.take_along_axis(r["p"], idx.astype(np.int64), axis=1)
+    used = sorted(set(int(e) for e in idx.ravel() if e < w.n_ffn))
+    remap = {e: i for i, e in enumerate(used)}
+    nU = len(used)
+    idx2 = np.array([[remap[e] if e < w.n_ffn else nU + (e - w.n_ffn) for e in row]
+                     for row in idx], np.int32)
+    d = O.dispatch(idx2, nU + w.n_zero)
+    n_rows = int(d["offsets"][nU])
+    xp = O.gather_rows(xs, d["perm"], w.top_k, n_rows)
+    yp = np.zeros((n_rows, w.d_model))
+    for i, e in enumerate(used):
+        lo, hi = int(d["offsets"][i]), int(d["offsets"][i + 1])
+        yp[lo:hi] = O.swiglu_ffn(xp[lo:hi], S.to_numpy64(m.wg[e]), S.to_numpy64(m.wu[e]),
+                                 S.to_numpy64(m.wd[e]))
+    return O.combine(xs, yp, idx2, gate, d["inv_perm"], nU)
+
+
+def full_oracle(m: Model, x_dev, gpu_idx=None):
+    w = m.w
+    return O.forward(S.to_numpy64(x_dev), S.to_numpy64(m.wr), m.bias.cpu().numpy(),
+                     S.to_numpy64(m.wg), S.to_numpy64(m.wu), S.to_numpy64(m.wd), w.n_ffn,
+                     w.top_k, w.routed_scaling,
+                     None if m.lb is None else m.lb.cpu().numpy().astype(np.float64),
+                     topk_idx=gpu_idx)
+
+
+def oracle_route(m: Model, x_dev):
+    w = m.w
+    return O.route(S.to_numpy64(x_dev), S.to_numpy64(m.wr), m.bias.cpu().numpy(), w.top_k,
+                   w.routed_scaling,
+                   None if m.lb is None else m.lb.cpu().numpy().astype(np.float64))
+
+
+# tolerances ---------------------------------------------------------------
+
+def tolerances(dtype: str):
+    """Output tolerance: max over tokens of the row relative L2 error
+    (1e-2 for bf16, 1e-5 for fp32).  Logit tolerance: fp32 accumulation of
+    exactly representable products over d_model terms."""
+    if dtype == "bf16":
+        return dict(y=1e-2, logits=1e-4, gate_rtol=1e-4)
+    return dict(y=1e-5, logits=1e-5, gate_rtol=1e-5)

@@ -1,0 +1,83 @@
+"""Host-side checks of the C-ABI library: it loads without a GPU, exports
+every entry point the header declares, sizes its workspace, and rejects bad
+arguments before touching the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_moe_layer_03_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 10, names
+    assert set(names) == set(B.ENTRY_POINTS)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_workspace_bytes():
+    s = B.make_shape(4096, 2048, 64, 32, 1024, 8, "bf16")
+    ws = B.moe_workspace_bytes(s)
+    Tk = 4096 * 8
+    # at least the H buffer (T*k rows of d_ff bf16) and the logits
+    assert ws >= Tk * 1024 * 2 + 4096 * 96 * 4
+    assert B.moe_workspace_bytes(B.make_shape(0, 2048, 64, 32, 1024, 8, "bf16")) == 0
+    assert B.moe_workspace_bytes(B.make_shape(16, 2000, 64, 32, 1024, 8, "bf16")) == 0
+
+
+@pytest.mark.parametrize("shape_args,code", [
+    ((0, 128, 8, 4, 256, 2, 0), -1),        # T < 1
+    ((64, 128, 0, 4, 256, 2, 0), -1),       # no FFN experts
+    ((64, 128, 8, 4, 256, 13, 0), -1),      # k > E
+    ((64, 128, 8, 4, 256, 2, 7), -2),       # dtype
+    ((64, 100, 8, 4, 256, 2, 0), -2),       # d_model % 64
+    ((64, 128, 8, 4, 200, 2, 0), -2),       # d_ff % 64
+    ((64, 128, 1000, 100, 256, 2, 0), -2),  # E > 1024
+    ((64, 128, 20, 4, 256, 17, 0), -2),     # k > 16
+])
+def test_invalid_shapes_rejected_before_any_gpu_work(shape_args, code):
+    s = B.MoeShape(*shape_args, 1.0)
+    L = B.lib()
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, fake, None, fake, None)
+    assert rc == code
+    assert L.moe_strerror(rc)
+
+
+def test_null_and_misaligned_pointers_rejected():
+    s = B.make_shape(64, 128, 8, 4, 256, 2, "f32")
+    L = B.lib()
+    a = ctypes.c_void_p(0x1000)
+    bad = ctypes.c_void_p(0x1004)
+    assert L.moe_route(ctypes.byref(s), None, a, None, a, a, a, None, a, None) == -1
+    assert L.moe_route(ctypes.byref(s), bad, a, None, a, a, a, None, a, None) == -5
+    assert L.moe_dispatch(ctypes.byref(s), a, None, a, a, a, a, None, None, None) == -1
+    assert L.moe_combine(ctypes.byref(s), a, a, a, a, a, None, None) == -1
+    assert L.moe_expert_ffn(ctypes.byref(s), a, None, None, a, a, a, a, a, a, None) == -1
+    s_bad = B.MoeShape(64, 128, 8, 4, 256, 2, 0, float("inf"))
+    assert L.moe_combine(ctypes.byref(s_bad), a, a, a, a, a, a, None) == -4
+
+
+def test_pid_rejects_nonfinite_params():
+    s = B.make_shape(64, 128, 8, 4, 256, 2, "f32")
+    L = B.lib()
+    a = ctypes.c_void_p(0x1000)
+    for bad in [B.MoePidParams(float("nan"), 0.01, 0.0, 0.0),
+                B.MoePidParams(6.0, float("inf"), 0.0, 0.0)]:
+        assert L.moe_pid_update(ctypes.byref(s), ctypes.byref(bad), a, a, a, None, 0, None) == -4
+    ok = B.MoePidParams(6.0, 0.01, 0.001, 0.0)
+    assert L.moe_pid_update(ctypes.byref(s), ctypes.byref(ok), None, a, a, None, 0, None) == -1
