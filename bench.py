@@ -1,0 +1,235 @@
+"""MoE layer forward benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: moe_route ->
+moe_dispatch -> moe_ffn_gate_up -> moe_ffn_down -> moe_combine, plus
+moe_pid_update on workloads that run the PID.  Inputs are resident in HBM
+before timing starts.  Prints ONE JSON line.
+
+The default workload is T=4096 tokens, d_model=2048, 64 SwiGLU experts
+(d_ff=1024) + 32 identity experts, top-8, bf16, router bias ~ N(0, 0.1),
+PID set point 6 real experts/token (Kp=0.01, Ki=0.001, Kd=0) updated after
+every batch; the timed steps are batches 0..K-1 of that run, starting from
+the initial bias (warm-up steps run first and are then undone).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA FLOP/s (MI355X)
+PEAK_F32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12       # B/s
+METRIC = "MoE-layer tokens/s at 1 GPU; % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="small_bf16",
+                    choices=["small_bf16", "decode_bf16", "prefill_bf16", "skewed_bf16",
+                             "tiny_f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def gate_up_units(w, A, U):
+    """Algorithmic work of one moe_ffn_gate_up launch.
+    flops: 2 GEMMs of A x d_model x d_ff.  bytes: gate+up weights of the U
+    touched experts, the A gathered token rows, and H written once."""
+    el = 2 if w.dtype == "bf16" else 4
+    flops = 4.0 * A * w.d_model * w.d_ff
+    byts = el * (2.0 * U * w.d_ff * w.d_model + A * w.d_model + A * w.d_ff)
+    return flops, byts
+
+
+def cpu_baseline(w, m, budget_s=12.0):
+    """Time the oracle (as it stands) on the host cores: whole batches of the
+    workload, in order, until about ``budget_s`` seconds of oracle work."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+    from sparse_moe_layer_03_amd import synth as S
+
+    wr = S.to_numpy64(m["wr"])
+    lb = None if m["lb"] is None else m["lb"].cpu().numpy().astype(np.float64)
+    bias = m["bias0"].cpu().numpy().astype(np.float64)
+    wg, wu, wd = S.to_numpy64(m["wg"]), S.to_numpy64(m["wu"]), S.to_numpy64(m["wd"])
+    st = O.PidState()
+    t_total, n_tok, nb = 0.0, 0, 0
+    while t_total < budget_s and nb < len(m["xs"]):
+        x = S.to_numpy64(m["xs"][nb])
+        t0 = time.perf_counter()
+        out = O.forward(x, wr, bias.astype(np.float32), wg, wu, wd, w.n_ffn, w.top_k,
+                        w.routed_scaling, lb)
+        if w.pid:
+            bias, st, _ = O.pid_update(out["counts"], w.n_ffn, x.shape[0], bias, st, *w.pid)
+        t_total += time.perf_counter() - t0
+        n_tok += x.shape[0]
+        nb += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return n_tok / t_total, threads, t_total, nb
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_moe_layer_03_amd import binding as B
+    from sparse_moe_layer_03_amd import synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    w = S.WORKLOADS[args.workload]
+    dt = S.torch_dtype(w.dtype)
+    alpha = None
+    if w.zipf_s:
+        with open(os.path.join(ROOT, "tests", "golden", "zipf_alpha.json")) as f:
+            alpha = json.load(f)["alpha"]
+
+    # ---- resident inputs
+    wr = S.make_router(w, dev)
+    bias0 = S.make_bias(w, dev)
+    bias = bias0.clone()
+    lb = S.zipf_logit_offset(w, alpha, dev) if w.zipf_s else None
+    wg, wu, wd = S.make_experts(w, dev)
+    n_x = min(max(args.steps, 1), 20) if w.pid else 1
+    xs = [S.make_x(w, b, dev) for b in range(n_x)]
+    shape = B.make_shape(w.T, w.d_model, w.n_ffn, w.n_zero, w.d_ff, w.top_k, w.dtype,
+                         w.routed_scaling)
+    buf = B.LayerBuffers(shape, dev)
+    params = B.MoePidParams(*w.pid) if w.pid else None
+    r_log = torch.zeros(max(args.steps, 1) + args.warmup + 1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        x = xs[i % len(xs)]
+        if ev is not None:
+            ev[0].record(stream)
+        B.moe_route(shape, x, wr, lb, bias, buf.topk_idx, buf.topk_gate, None, buf.ws)
+        if ev is not None:
+            ev[1].record(stream)
+        B.moe_dispatch(shape, buf.topk_idx, x, buf.counts, buf.offsets, buf.perm,
+                       buf.inv_perm, None, buf.ws)
+        if ev is not None:
+            ev[2].record(stream)
+        B.moe_ffn_gate_up(shape, x, None, buf.perm, buf.offsets, wg, wu, buf.ws)
+        if ev is not None:
+            ev[3].record(stream)
+        B.moe_ffn_down(shape, buf.offsets, wd, buf.y_perm, buf.ws)
+        if ev is not None:
+            ev[4].record(stream)
+        B.moe_combine(shape, x, buf.y_perm, buf.topk_idx, buf.topk_gate, buf.inv_perm, buf.y)
+        if ev is not None:
+            ev[5].record(stream)
+        if params is not None:
+            B.moe_pid_update(shape, params, buf.counts, buf.pid_state, bias, r_log,
+                             r_log.numel())
+        if ev is not None:
+            ev[6].record(stream)
+
+    # ---- warm-up, then restore the initial controller state
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    bias.copy_(bias0)
+    buf.pid_state.zero_()
+    r_log.zero_()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    # ---- per-stage durations (HIP events on the launch stream)
+    names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine", "pid"]
+    st_ms = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]
+             for j, n in enumerate(names)}
+    counts = buf.counts.cpu().numpy()
+    if w.pid:
+        A = np.rint(r_log.cpu().numpy()[:K] * w.T).astype(np.int64)
+        U = np.full(K, int((counts[: w.n_ffn] > 0).sum()))  # last batch's touched experts
+    else:
+        A = np.full(K, int(counts[: w.n_ffn].sum()))
+        U = np.full(K, int((counts[: w.n_ffn] > 0).sum()))
+    fl, by = zip(*[gate_up_units(w, int(a), int(u)) for a, u in zip(A, U)])
+    gu_s = np.array(st_ms["ffn_gate_up"]) / 1e3
+    peak_fl = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32_MFMA
+    t_fl = np.sum(fl) / peak_fl
+    t_by = np.sum(by) / PEAK_HBM
+    if t_fl >= t_by:
+        roof = {"bound": "mfma", "achieved": float(np.sum(fl) / gu_s.sum() / 1e12),
+                "peak": peak_fl / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": float(np.sum(by) / gu_s.sum() / 1e9),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel (gate/up + SwiGLU), mean %.4f ms/launch" % (
+        gu_s.mean() * 1e3)
+
+    tokens = w.T * K
+    value = tokens / elapsed
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/d_in) weights)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d_model, "n_ffn": w.n_ffn,
+                   "n_zero": w.n_zero, "d_ff": w.d_ff, "top_k": w.top_k,
+                   "pid": list(w.pid) if w.pid else None},
+        "roofline": roof,
+        "stages_ms_mean": {n: float(np.mean(v)) for n, v in st_ms.items()},
+        "ffn_assignments_per_step_mean": float(np.mean(A)),
+    }
+    if w.pid:
+        line["r_per_step"] = [round(float(v), 4) for v in r_log.cpu().numpy()[:K]]
+
+    if not args.no_cpu_baseline and w.name in ("small_bf16", "skewed_bf16", "tiny_f32"):
+        m = dict(wr=wr, lb=lb, bias0=bias0, wg=wg, wu=wu, wd=wd, xs=xs)
+        v, threads, secs, nb = cpu_baseline(w, m)
+        line["cpu_baseline"] = {
+            "value": v, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {nb} whole batch(es) ({nb * w.T} tokens) of the same workload "
+                      f"and inputs: oracle route+dispatch+FFN+combine"
+                      f"{'+PID' if w.pid else ''} in float64, {secs:.1f} s"}
+    else:
+        # the decode/prefill model (38.7 GB bf16) does not fit a float64 host copy
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
