@@ -1,7 +1,7 @@
 """Summarise a rocprofv3 results database (rocpd SQLite) per kernel:
 calls, total/average/min/max duration.  Reads only the database file.
 
-    python profiles/rocpd_stats.py path/to/results.db [name-substring]
+    python -m sparse_moe_layer_03_amd.rocpd_stats path/to/results.db [name-substring]
 """
 import sqlite3
 import sys
