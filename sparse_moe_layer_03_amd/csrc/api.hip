@@ -80,6 +80,15 @@ static WsLayout ws_layout(const moe_shape* s) {
   return w;
 }
 
+// The direct-to-LDS kernel addresses operands with 32-bit byte offsets and
+// walks K in pairs of 64-element steps.
+static bool big_kernel_ok(const moe_shape* s, int K) {
+  const size_t Tk = (size_t)s->T * s->top_k;
+  return s->dtype == MOE_BF16 && K % 128 == 0 &&
+         (size_t)s->T * s->d_model * 2 < (1ull << 32) && Tk * s->d_ff * 2 < (1ull << 32) &&
+         (size_t)s->d_ff * s->d_model * 2 < (1ull << 32);
+}
+
 // Few rows per expert -> 16-row tiles; otherwise 128x128 tiles.
 static int ffn_big_tiles(const moe_shape* s) {
   const long E = (long)s->n_ffn + s->n_zero;
@@ -189,6 +198,8 @@ int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const
   g.M = s->T;
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
+  if (ffn_big_tiles(s) && big_kernel_ok(s, s->d_model))
+    return launch_gemm_big(1, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 
@@ -207,6 +218,9 @@ int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down,
   g.K = s->d_ff;
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
+  g.M = s->T;
+  if (ffn_big_tiles(s) && big_kernel_ok(s, s->d_ff))
+    return launch_gemm_big(2, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 

@@ -116,7 +116,13 @@ grouped_gemm_kernel(GemmArgs g) {
     const int grp = lo;
     const int mt_g = s_mt[grp + 1] - s_mt[grp];
     const long local = t - (long)s_mt[grp] * ntiles;
-    const int nt = (int)(local / mt_g), mi = (int)(local % mt_g);
+    // groups of 4 m-tiles x all n-tiles, n-tile major inside a group, so
+    // tiles running together on one XCD share rows and weights in L2
+    constexpr int MG = 4;
+    const int grp_m0 = (int)(local / ((long)MG * ntiles)) * MG;
+    const int mg = min(MG, mt_g - grp_m0);
+    const int in_grp = (int)(local - (long)grp_m0 * ntiles);
+    const int nt = in_grp / mg, mi = grp_m0 + in_grp % mg;
     const int row0 = (MODE == MODE_ROUTER) ? 0 : g.offsets[grp];
     const int rows = (MODE == MODE_ROUTER) ? g.M : (g.offsets[grp + 1] - row0);
     const int m0 = mi * BM;
@@ -171,8 +177,10 @@ grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    u32x4_t ra[A_IT], rb[B_IT];
-    auto gload = [&](int ks) {
+    // Two register sets carry the global loads of the next two K-steps, so a
+    // load has two K-steps of MFMA work to arrive before it is written to LDS.
+    u32x4_t ra0[A_IT], rb0[B_IT], ra1[A_IT], rb1[B_IT];
+    auto gload = [&](u32x4_t* ra, u32x4_t* rb, int ks) {
       const size_t off = (size_t)ks * 128;
 #pragma unroll
       for (int it = 0; it < A_IT; ++it)
@@ -181,7 +189,7 @@ grouped_gemm_kernel(GemmArgs g) {
       for (int it = 0; it < B_IT; ++it)
         if (tid + it * NT < B_CH) rb[it] = ld16(b_src[it] + off);
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](const u32x4_t* ra, const u32x4_t* rb, int buf) {
 #pragma unroll
       for (int it = 0; it < A_IT; ++it)
         if (tid + it * NT < A_CH) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_lds[it]]) = ra[it];
@@ -189,13 +197,7 @@ grouped_gemm_kernel(GemmArgs g) {
       for (int it = 0; it < B_IT; ++it)
         if (tid + it * NT < B_CH) *reinterpret_cast<u32x4_t*>(&s_b[buf][b_lds[it]]) = rb[it];
     };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int ks = 0; ks < nK; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < nK) gload(ks + 1);
+    auto compute = [&](int buf) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int c = kk * 4 + kg;
@@ -220,7 +222,23 @@ grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::step(af[i], bfr[j], acc[i][j]);
       }
-      if (ks + 1 < nK) lstore(buf ^ 1);
+    };
+
+    gload(ra0, rb0, 0);
+    if (nK > 1) gload(ra1, rb1, 1);
+    lstore(ra0, rb0, 0);
+    __syncthreads();
+    for (int ks = 0; ks < nK; ks += 2) {
+      // LDS stage 0 holds step ks; registers set 1 hold step ks+1 (in flight)
+      if (ks + 2 < nK) gload(ra0, rb0, ks + 2);
+      compute(0);
+      if (ks + 1 < nK) lstore(ra1, rb1, 1);
+      __syncthreads();
+      if (ks + 1 >= nK) break;
+      // LDS stage 1 holds step ks+1; registers set 0 hold step ks+2
+      if (ks + 3 < nK) gload(ra1, rb1, ks + 3);
+      compute(1);
+      if (ks + 2 < nK) lstore(ra0, rb0, 0);
       __syncthreads();
     }
 
@@ -279,19 +297,28 @@ static int launch_cfg(const GemmArgs& g, hipStream_t st) {
   return check_launch();
 }
 
+// Tile shapes (rows x weight-rows, waves along M x N).  Overridable at build
+// time for tuning sweeps.
+#ifndef MOE_BIG_TILE
+#define MOE_BIG_TILE 128, 128, 2, 2
+#endif
+#ifndef MOE_SMALL_TILE
+#define MOE_SMALL_TILE 16, 128, 1, 4
+#endif
+
 template <typename T>
 static int launch_typed(int mode, int big, const GemmArgs& g, hipStream_t st) {
   if (big) {
     switch (mode) {
-      case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, 128, 128, 2, 2>(g, st);
-      case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, 128, 128, 2, 2>(g, st);
-      default: return launch_cfg<T, MODE_DOWN, 128, 128, 2, 2>(g, st);
+      case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, MOE_BIG_TILE>(g, st);
+      case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, MOE_BIG_TILE>(g, st);
+      default: return launch_cfg<T, MODE_DOWN, MOE_BIG_TILE>(g, st);
     }
   }
   switch (mode) {
-    case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, 16, 128, 1, 4>(g, st);
-    case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, 16, 128, 1, 4>(g, st);
-    default: return launch_cfg<T, MODE_DOWN, 16, 128, 1, 4>(g, st);
+    case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, MOE_SMALL_TILE>(g, st);
+    case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, MOE_SMALL_TILE>(g, st);
+    default: return launch_cfg<T, MODE_DOWN, MOE_SMALL_TILE>(g, st);
   }
 }
 

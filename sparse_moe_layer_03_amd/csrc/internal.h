@@ -27,6 +27,9 @@ struct GemmArgs {
 // 16-row tiles for few rows per expert.
 int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st);
 
+// bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles.
+int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st);
+
 int launch_topk(const float* logits, const float* bias, int T, int E, int k,
                 float scaling, int32_t* idx, float* gate, hipStream_t st);
 

@@ -61,6 +61,7 @@ def test_small_bf16_workload_batch0():
     (600, 192, 32, 8, 320, 4),     # 128x128 tiles (>= 32 rows per expert)
     (77, 256, 40, 24, 192, 6),     # 16-row tiles
     (1, 64, 3, 1, 64, 2),          # single token
+    (1000, 384, 16, 8, 384, 4),    # bf16: 256x256 direct-to-LDS tiles, 2 m-tiles/expert
 ])
 def test_ragged_shapes(dtype, shape):
     T, d, N, Z, dff, k = shape
