@@ -6,19 +6,21 @@
 //    a few independent accumulators (the 16x16x32 form needs many waves or
 //    accumulators per SIMD to hide its latency).  A 16-byte chunk of an
 //    operand row is the 8 bf16 one lane supplies; lanes 0-31 and 32-63 take
-//    neighbouring chunks, so a 128-byte LDS row feeds four MFMA K-steps.
+//    neighbouring chunks, so a stage row of CK chunks feeds CK/2 MFMA K-steps.
 //  * Operand tiles move HBM -> LDS with the direct-to-LDS load
 //    (global_load_lds_dwordx4): no staging registers or ds_write.  One wave
-//    instruction fills a contiguous KiB (8 rows x 128 B), so each lane
-//    fetches the chunk that the row's XOR swizzle places in its slot; the
-//    swizzle (chunk ^ (row & 7)) keeps the 32-row fragment reads free of bank
-//    conflicts.
-//  * NS named LDS stages (one array each) and a K loop unrolled by NS: the
+//    instruction fills a contiguous KiB of stage rows, so each lane fetches
+//    the chunk that the row's XOR swizzle places in its slot; the swizzle
+//    keeps the 32-row fragment reads free of bank conflicts.
+//  * NS named LDS stages (one array each, K-steps of 32 or 64) and a K loop
+//    unrolled by NS, NS-1 stages in flight: the
 //    compiler can then prove that the stage being read is not the one being
 //    filled, and no vmcnt wait separates them.  Each K-step waits (vmcnt)
 //    only for its own stage, then one s_barrier.
 //  * Balanced tile heights: an expert with m rows gets ceil(m / BM) tiles of
 //    equal height, so a tile never holds a lone remainder of a few rows.
+//  * 256 x 256 tiles over 8 waves (2 per SIMD) of 128 x 64: one wave's MFMAs
+//    run while the other waits on LDS or DMA.
 //  * Persistent grid, device-side tile list, XCD-contiguous tile order (as in
 //    gemm.hip).
 
@@ -45,28 +47,44 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int NS, int TA, int MG>
+// Swizzle of the 16-byte chunk c of tile row r inside a stage whose rows hold
+// CK chunks: 8-chunk rows XOR with (r ^ (r >> 3)) & 7, 4-chunk rows with
+// ((r >> 1) ^ (r >> 3)) & 3.  Either keeps every 8-lane group (32 banks) and
+// every 16-lane group (64 banks) of a 32-row fragment read on distinct banks.
+template <int CK>
+__device__ __forceinline__ int swz(int r, int c) {
+  if (CK == 8) return c ^ ((r ^ (r >> 3)) & 7);
+  return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+template <int MODE, int BM, int BN, int WM, int WN, int NS, int CK, int MG>
 __global__ void __launch_bounds__(64 * WM * WN, 1)
 grouped_gemm_big_kernel(GemmArgs g) {
   constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int RB = CK * 16;                       // bytes per stage row
+  constexpr int RPK = 1024 / RB;                    // rows per KiB
+  constexpr int KS = CK * 8;                        // K elements per stage
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;       // 32x32 blocks per wave
   constexpr int HN = (MODE == 1) ? BN / 2 : BN;     // output columns per tile
-  constexpr int A_KB = BM / 8, B_KB = BN / 8;        // KiB chunks per stage
+  constexpr int A_KB = BM / RPK, B_KB = BN / RPK;    // KiB chunks per stage
   static_assert(A_KB % NW == 0 && B_KB % NW == 0, "chunks per wave");
   constexpr int A_PW = A_KB / NW, B_PW = B_KB / NW;  // DMA instructions per wave
   constexpr int L = A_PW + B_PW;
-  static_assert(NS == 2 || NS == 3, "two or three stages");
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  static_assert(CK == 4 || CK == 8, "64- or 128-byte stage rows");
   static_assert(L * (NS - 1) < 64, "vmcnt range");
   static_assert(MODE != 1 || NB % 2 == 0, "gate/up pairing");
 
   // One array per stage (see the header comment).
-  __shared__ __attribute__((aligned(1024))) char s_a0[BM * 128];
-  __shared__ __attribute__((aligned(1024))) char s_a1[BM * 128];
-  __shared__ __attribute__((aligned(1024))) char s_a2[NS == 3 ? BM * 128 : 16];
-  __shared__ __attribute__((aligned(1024))) char s_b0[BN * 128];
-  __shared__ __attribute__((aligned(1024))) char s_b1[BN * 128];
-  __shared__ __attribute__((aligned(1024))) char s_b2[NS == 3 ? BN * 128 : 16];
+  __shared__ __attribute__((aligned(1024))) char s_a0[BM * RB];
+  __shared__ __attribute__((aligned(1024))) char s_a1[BM * RB];
+  __shared__ __attribute__((aligned(1024))) char s_a2[NS >= 3 ? BM * RB : 16];
+  __shared__ __attribute__((aligned(1024))) char s_a3[NS >= 4 ? BM * RB : 16];
+  __shared__ __attribute__((aligned(1024))) char s_b0[BN * RB];
+  __shared__ __attribute__((aligned(1024))) char s_b1[BN * RB];
+  __shared__ __attribute__((aligned(1024))) char s_b2[NS >= 3 ? BN * RB : 16];
+  __shared__ __attribute__((aligned(1024))) char s_b3[NS >= 4 ? BN * RB : 16];
   __shared__ int s_mt[kBigMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
 
@@ -103,13 +121,14 @@ grouped_gemm_big_kernel(GemmArgs g) {
   const long total = (long)s_mt[ngroups] * ntiles;
   const int G = gridDim.x, b = blockIdx.x;
   const int vid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  const int nK = g.K / 64;
+  const int nK = g.K / KS;  // the host guarantees nK % NS == 0
   const size_t row_bytes = (size_t)g.K * 2;
 
-  // DMA lane geometry: lane fills slot (lane & 7) of row (lane >> 3) of a KiB
-  const int dma_row = lane >> 3;
-  const int dma_chunk = (lane & 7) ^ dma_row;  // logical chunk stored in that slot
-  uint32_t tsink = 0;
+  // DMA lane geometry: lane fills slot (lane % CK) of row (lane / CK) of a
+  // KiB and fetches the logical chunk that the swizzle of that tile row
+  // stores in the slot (the swizzle is an involution in c for a fixed row).
+  const int dma_row = lane / CK;
+  const int dma_slot = lane % CK;
 
   for (long t = vid; t < total; t += G) {
     int lo = 0, hi = ngroups - 1;
@@ -139,7 +158,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     uint32_t a_off[A_PW];
 #pragma unroll
     for (int q = 0; q < A_PW; ++q) {
-      const int r = (wave + q * NW) * 8 + dma_row;  // tile row
+      const int r = (wave + q * NW) * RPK + dma_row;  // tile row
       int rr = m0 + r;
       if (rr > m_end - 1) rr = m_end - 1;
       long src_row;
@@ -149,7 +168,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       } else {
         src_row = row0 + rr;
       }
-      a_off[q] = (uint32_t)(src_row * row_bytes) + dma_chunk * 16;
+      a_off[q] = (uint32_t)(src_row * row_bytes) + swz<CK>(r, dma_slot) * 16;
     }
     const char* b_base0 = (const char*)g.b0 + (size_t)grp * g.N * row_bytes;
     const char* b_base1 =
@@ -157,35 +176,11 @@ grouped_gemm_big_kernel(GemmArgs g) {
     uint32_t b_off[B_PW];
 #pragma unroll
     for (int q = 0; q < B_PW; ++q) {
-      const int r = (wave + q * NW) * 8 + dma_row;
+      const int r = (wave + q * NW) * RPK + dma_row;
       int n = (MODE == 1 && r >= HN) ? n0 + r - HN : n0 + r;
       if (n > g.N - 1) n = g.N - 1;
-      b_off[q] = (uint32_t)(n * row_bytes) + dma_chunk * 16;
+      b_off[q] = (uint32_t)(n * row_bytes) + swz<CK>(r, dma_slot) * 16;
     }
-
-    // L2 touch-ahead: thread tid owns row tid of the A tile and of the B tile
-    // and loads one dword of that row's 128-byte segment TA steps ahead, so
-    // the DMA of that step later hits L2 instead of HBM / MALL.
-    uint32_t ta_off = 0, tb_off = 0;
-    const char* tb_base = b_base0;
-    if (TA > 0) {
-      int rr = m0 + (tid < BM ? tid : BM - 1);
-      if (rr > m_end - 1) rr = m_end - 1;
-      long src_row;
-      if (MODE == 1 && g.perm != nullptr) {
-        src_row = g.perm[row0 + rr] / g.top_k;
-        if (src_row < 0 || src_row >= g.M) src_row = 0;
-      } else {
-        src_row = row0 + rr;
-      }
-      ta_off = (uint32_t)(src_row * row_bytes);
-      const int r = tid < BN ? tid : BN - 1;
-      int n = (MODE == 1 && r >= HN) ? n0 + r - HN : n0 + r;
-      if (n > g.N - 1) n = g.N - 1;
-      tb_off = (uint32_t)(n * row_bytes);
-      tb_base = (MODE == 1 && r >= HN) ? b_base1 : b_base0;
-    }
-    uint32_t tv[2][2] = {{0u, 0u}, {0u, 0u}};
 
     f32x16_t acc[MB][NB];
 #pragma unroll
@@ -195,11 +190,11 @@ grouped_gemm_big_kernel(GemmArgs g) {
 
     auto stage_a = [&](auto bufc) -> char* {
       constexpr int BUF = decltype(bufc)::value;
-      return BUF == 0 ? s_a0 : (BUF == 1 ? s_a1 : s_a2);
+      return BUF == 0 ? s_a0 : (BUF == 1 ? s_a1 : (BUF == 2 ? s_a2 : s_a3));
     };
     auto stage_b = [&](auto bufc) -> char* {
       constexpr int BUF = decltype(bufc)::value;
-      return BUF == 0 ? s_b0 : (BUF == 1 ? s_b1 : s_b2);
+      return BUF == 0 ? s_b0 : (BUF == 1 ? s_b1 : (BUF == 2 ? s_b2 : s_b3));
     };
 
     // every stage issues exactly L loads per wave (the vmcnt waits count on
@@ -207,7 +202,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     auto issue = [&](auto bufc, int ks) {
       char* sa = stage_a(bufc);
       char* sb = stage_b(bufc);
-      const size_t off = (size_t)ks * 128;
+      const size_t off = (size_t)ks * RB;
 #pragma unroll
       for (int q = 0; q < A_PW; ++q) {
         const int kb = wave + q * NW;
@@ -218,7 +213,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       for (int q = 0; q < B_PW; ++q) {
         const int kb = wave + q * NW;
         // gate rows fill the first half of the B tile, up rows the second
-        const char* bb = (MODE == 1 && kb * 8 >= HN) ? b_base1 : b_base0;
+        const char* bb = (MODE == 1 && kb * RPK >= HN) ? b_base1 : b_base0;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
                                          (lds_void_t*)(sb + kb * 1024), 16, 0, 0);
       }
@@ -239,50 +234,35 @@ grouped_gemm_big_kernel(GemmArgs g) {
       constexpr int BUF = decltype(bufc)::value;
       const char* sa = stage_a(bufc);
       const char* sb = stage_b(bufc);
-      // loads newer than this stage's DMA: the next stage (NS == 3) and the
-      // touches issued after it in the previous step (TA > 0)
-      const bool prev_touch = TA > 0 && ks >= 1 && ks - 1 + TA < nK;
-      if (NS == 3 && ks + 1 < nK) {
-        if (prev_touch) wait_vmcnt<(NS == 3 ? L + 2 : 0)>();
-        else wait_vmcnt<(NS == 3 ? L : 0)>();
-      } else {
-        if (prev_touch) wait_vmcnt<2>();
-        else wait_vmcnt<0>();
-      }
+      // stages newer than this one that may still be in flight
+      const int ahead = min(NS - 2, nK - 1 - ks);
+      if (NS >= 4 && ahead >= 2) wait_vmcnt<(NS >= 4 ? 2 * L : 0)>();
+      else if (NS >= 3 && ahead >= 1) wait_vmcnt<(NS >= 3 ? L : 0)>();
+      else wait_vmcnt<0>();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
       if (ks + NS - 1 < nK) issue(std::integral_constant<int, (BUF + NS - 1) % NS>{}, ks + NS - 1);
-      if (TA > 0) {
-        // the touches of two steps ago have landed (they precede this stage's
-        // DMA); fold them into a sink so the loads are not dead
-        tsink ^= tv[BUF & 1][0] ^ tv[BUF & 1][1];
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + TA < nK) {
-          const size_t toff = (size_t)(ks + TA) * 128;
-          tv[BUF & 1][0] = *(const uint32_t*)(a_base + ta_off + toff);
-          tv[BUF & 1][1] = *(const uint32_t*)(tb_base + tb_off + toff);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
+      // favour this wave's MFMA issue over the other wave on the SIMD
+      __builtin_amdgcn_s_setprio(1);
       u32x4_t af[2][MB], bfr[2][NB];
       auto load = [&](int set, int kk) {
         const int c = kk * 2 + kg;
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int r = (i * WM + wm) * 32 + r32;
-          af[set][i] = *reinterpret_cast<const u32x4_t*>(&sa[r * 128 + ((c ^ (r & 7)) << 4)]);
+          af[set][i] = *reinterpret_cast<const u32x4_t*>(&sa[r * RB + (swz<CK>(r, c) << 4)]);
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int r = brow(j);
-          bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * 128 + ((c ^ (r & 7)) << 4)]);
+          bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * RB + (swz<CK>(r, c) << 4)]);
         }
       };
+      constexpr int NKK = CK / 2;  // MFMA K-slices of 16 per stage
       load(0, 0);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk + 1 < 4) load((kk + 1) & 1, kk + 1);
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) load((kk + 1) & 1, kk + 1);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -291,6 +271,25 @@ grouped_gemm_big_kernel(GemmArgs g) {
                 __builtin_bit_cast(bf16x8_t, bfr[kk & 1][j]),
                 __builtin_bit_cast(bf16x8_t, af[kk & 1][i]), acc[i][j], 0, 0, 0);
       }
+      // Pin the schedule (the default one sinks every LDS read next to its
+      // first use and stalls on it): the first slice's reads, then each
+      // slice's MFMAs with the next slice's reads interleaved 1:1 at the
+      // front, so they have landed before that slice starts.
+      constexpr int NR = MB + NB;        // LDS reads per slice
+      constexpr int NM = MB * NB;        // MFMAs per slice
+      static_assert(NM >= NR, "read/MFMA interleave");
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+      for (int kk = 0; kk + 1 < NKK; ++kk) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+      __builtin_amdgcn_s_setprio(0);
     };
 
     // previous tile's epilogue stores and LDS reads must be done before the
@@ -299,15 +298,14 @@ grouped_gemm_big_kernel(GemmArgs g) {
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     issue(std::integral_constant<int, 0>{}, 0);
-    if (NS == 3 && nK > 1) issue(std::integral_constant<int, 1>{}, 1);
-    int ks = 0;
-    for (; ks + NS <= nK; ks += NS) {
+    if (NS >= 3 && nK > 1) issue(std::integral_constant<int, 1>{}, 1);
+    if (NS >= 4 && nK > 2) issue(std::integral_constant<int, 2>{}, 2);
+    for (int ks = 0; ks < nK; ks += NS) {
       kstep(std::integral_constant<int, 0>{}, ks);
       kstep(std::integral_constant<int, 1>{}, ks + 1);
-      if (NS == 3) kstep(std::integral_constant<int, NS - 1>{}, ks + 2);
+      if (NS >= 3) kstep(std::integral_constant<int, (NS >= 3 ? 2 : 0)>{}, ks + 2);
+      if (NS >= 4) kstep(std::integral_constant<int, (NS >= 4 ? 3 : 0)>{}, ks + 3);
     }
-    if (ks < nK) kstep(std::integral_constant<int, 0>{}, ks);
-    if (ks + 1 < nK) kstep(std::integral_constant<int, 1>{}, ks + 1);
 
     // ---- epilogue.  Weights were the MFMA row operand, so block (i, j) is
     // C^T: lane (r32, kg) holds, for quad q = v / 4, the 4 consecutive output
@@ -357,16 +355,15 @@ grouped_gemm_big_kernel(GemmArgs g) {
       }
     }
   }
-  // the touch sink is a data dependency only; ngroups is never negative
-  if (TA > 0 && g.ngroups < 0) ((uint32_t*)g.c)[tid] = tsink;
 }
 
 #ifndef MOE_HUGE_TILE
-#define MOE_HUGE_TILE 256, 256, 2, 2, 2, 0, 4
+#define MOE_HUGE_TILE 256, 256, 2, 4, 2, 8, 4
 #endif
 
-template <int BM, int BN, int WM, int WN, int NS, int TA, int MG>
+template <int BM, int BN, int WM, int WN, int NS, int CK, int MG>
 struct BigCfg {
+  static constexpr int KSTEP_MULT = NS * CK * 8;  // K must be a multiple of this
   static constexpr int NT = 64 * WM * WN;
 };
 
