@@ -70,8 +70,9 @@ static WsLayout ws_layout(const moe_shape* s) {
   const size_t Tk = (size_t)s->T * s->top_k;
   WsLayout w;
   size_t off = 0;
-  w.logits = off;
-  off = up256(off + (size_t)s->T * E * sizeof(float));
+  w.logits = off;  // K-split partial logits
+  off = up256(off + (size_t)router_ksplit(s->T, (int)E, s->d_model, s->dtype) * s->T * E *
+                        sizeof(float));
   w.hist = off;
   off = up256(off + E * (size_t)dispatch_blocks((long)Tk) * sizeof(int32_t));
   w.h = off;
@@ -95,10 +96,11 @@ static int ffn_big_tiles(const moe_shape* s) {
   return ((long)s->T * s->top_k) / E >= 32;
 }
 
-static int router_big_tiles(const moe_shape* s, int cus) {
-  const long E = (long)s->n_ffn + s->n_zero;
-  const long tiles = ((long)s->T / 128) * ((E + 127) / 128);
-  return tiles >= cus;
+// 128x128 router tiles when there are enough of them (prefill), else 16-row
+// tiles with a split K loop.
+static int router_big_tiles(const moe_shape* s) {
+  const int E = s->n_ffn + s->n_zero;
+  return router_ksplit(s->T, E, s->d_model, s->dtype) == 1 && (long)(s->T / 128) * ((E + 127) / 128) >= 256;
 }
 
 }  // namespace moe
@@ -131,28 +133,28 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
               void* stream) {
   int rc = check_shape(s);
   if (rc) return rc;
-  if (!x || !w_router || !bias || !topk_idx || !topk_gate || (!logits_out && !ws)) return MOE_EINVAL;
-  if (!al16(x) || !al16(w_router) || (ws && !al16(ws)) || !al4(bias) || !al4(topk_idx) ||
+  if (!x || !w_router || !bias || !topk_idx || !topk_gate || !ws) return MOE_EINVAL;
+  if (!al16(x) || !al16(w_router) || !al16(ws) || !al4(bias) || !al4(topk_idx) ||
       !al4(topk_gate) || (logit_bias && !al4(logit_bias)) || (logits_out && !al4(logits_out)))
     return MOE_EALIGN;
-  const int cus = device_cu_count();
-  if (cus <= 0) return MOE_EHIP;
   hipStream_t st = (hipStream_t)stream;
   const int E = s->n_ffn + s->n_zero;
-  float* logits = logits_out ? logits_out : (float*)((char*)ws + ws_layout(s).logits);
+  const int nsplit = router_ksplit(s->T, E, s->d_model, s->dtype);
+  float* partials = (float*)((char*)ws + ws_layout(s).logits);
   GemmArgs g{};
   g.a = x;
   g.b0 = w_router;
-  g.c = logits;
-  g.col_bias = logit_bias;
+  g.c = partials;
   g.M = s->T;
   g.N = E;
   g.K = s->d_model;
   g.ngroups = 1;
   g.top_k = s->top_k;
-  rc = launch_gemm(s->dtype, 0, router_big_tiles(s, cus), g, st);
+  g.ksplit = nsplit;
+  rc = launch_gemm(s->dtype, 0, router_big_tiles(s), g, st);
   if (rc) return rc;
-  return launch_topk(logits, bias, s->T, E, s->top_k, s->routed_scaling, topk_idx, topk_gate, st);
+  return launch_topk(partials, nsplit, logit_bias, logits_out, bias, s->T, E, s->top_k,
+                     s->routed_scaling, topk_idx, topk_gate, st);
 }
 
 int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* counts,
@@ -198,6 +200,7 @@ int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const
   g.M = s->T;
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
+  g.ksplit = 1;
   if (ffn_big_tiles(s) && big_kernel_ok(s, s->d_model))
     return launch_gemm_big(1, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
@@ -219,6 +222,7 @@ int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down,
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
   g.M = s->T;
+  g.ksplit = 1;
   if (ffn_big_tiles(s) && big_kernel_ok(s, s->d_ff))
     return launch_gemm_big(2, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);

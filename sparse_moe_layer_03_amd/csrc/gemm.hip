@@ -99,14 +99,18 @@ grouped_gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
   const int ntiles = (g.N + HN - 1) / HN;
-  const long total = (long)s_mt[ngroups] * ntiles;
+  const int ksplit = (MODE == MODE_ROUTER) ? g.ksplit : 1;
+  const long total = (long)s_mt[ngroups] * ntiles * ksplit;
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int vid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  const int nK = g.K / BK;
+  const int nK = g.K / BK / ksplit;  // K-steps per split (the host divides evenly)
   const size_t a_row_bytes = (size_t)g.K * sizeof(T);
 
-  for (long t = vid; t < total; t += G) {
+  for (long tt = vid; tt < total; tt += G) {
+    const int split = (int)(tt % ksplit);
+    const long t = tt / ksplit;
+    const size_t k_off = (size_t)split * nK * 128;  // byte offset of this split's K range
     // locate group: last gi with s_mt[gi] * ntiles <= t
     int lo = 0, hi = ngroups - 1;
     while (lo < hi) {
@@ -181,7 +185,7 @@ grouped_gemm_kernel(GemmArgs g) {
     // load has two K-steps of MFMA work to arrive before it is written to LDS.
     u32x4_t ra0[A_IT], rb0[B_IT], ra1[A_IT], rb1[B_IT];
     auto gload = [&](u32x4_t* ra, u32x4_t* rb, int ks) {
-      const size_t off = (size_t)ks * 128;
+      const size_t off = k_off + (size_t)ks * 128;
 #pragma unroll
       for (int it = 0; it < A_IT; ++it)
         if (tid + it * NT < A_CH) ra[it] = ld16(a_src[it] + off);
@@ -263,9 +267,8 @@ grouped_gemm_kernel(GemmArgs g) {
           for (int j = 0; j < NB; ++j) {
             const int col = n0 + wn * WTN + j * 16 + r16;
             if (col < g.N) {
-              if (MODE == MODE_ROUTER)
-                ((float*)g.c)[(size_t)r * g.N + col] =
-                    acc[i][j][v] + (g.col_bias != nullptr ? g.col_bias[col] : 0.f);
+              if (MODE == MODE_ROUTER)  // partial sum of this K split
+                ((float*)g.c)[((size_t)split * g.M + r) * g.N + col] = acc[i][j][v];
               else
                 ((T*)g.c)[(size_t)(row0 + r) * g.N + col] = ElemOps<T>::from_f(acc[i][j][v]);
             }

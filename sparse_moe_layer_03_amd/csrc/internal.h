@@ -21,6 +21,7 @@ struct GemmArgs {
   int K;                   // reduction length: d_model | d_model | d_ff
   int ngroups;             // experts (grouped modes)
   int top_k;
+  int ksplit;              // router: K is split into this many partial sums
 };
 
 // mode: 0 router, 1 gate/up + SwiGLU, 2 down.  big: 128x128 tiles, else
@@ -30,8 +31,14 @@ int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st)
 // bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles.
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st);
 
-int launch_topk(const float* logits, const float* bias, int T, int E, int k,
-                float scaling, int32_t* idx, float* gate, hipStream_t st);
+// partials: nsplit slices of [T, E] fp32 summed in slice order, plus
+// col_bias (nullable); logits_out (nullable) receives the sum.
+int launch_topk(const float* partials, int nsplit, const float* col_bias, float* logits_out,
+                const float* bias, int T, int E, int k, float scaling, int32_t* idx, float* gate,
+                hipStream_t st);
+
+// K split of the router GEMM for a shape (depends on the shape only).
+int router_ksplit(int T, int E, int d_model, int dtype);
 
 int launch_dispatch(const int32_t* idx, int Tk, int E, int nb, int32_t* block_hist,
                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,

@@ -21,19 +21,28 @@ namespace moe {
 
 template <int PL>
 __global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, int T, int E,
+topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restrict__ col_bias,
+            float* __restrict__ logits_out, const float* __restrict__ bias, int T, int E,
             int k, float scaling, int32_t* __restrict__ idx, float* __restrict__ gate) {
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
-  const float* row = logits + (size_t)t * E;
 
+  // logits = sum of the K-split partials in split order (+ classifier offset)
   float l[PL];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     const int e = lane + 64 * i;
-    l[i] = (e < E) ? row[e] : -INFINITY;
+    if (e < E) {
+      float v = partials[(size_t)t * E + e];
+      for (int sp = 1; sp < nsplit; ++sp) v += partials[((size_t)sp * T + t) * E + e];
+      if (col_bias != nullptr) v += col_bias[e];
+      if (logits_out != nullptr) logits_out[(size_t)t * E + e] = v;
+      l[i] = v;
+    } else {
+      l[i] = -INFINITY;
+    }
     m = fmaxf(m, l[i]);
   }
   m = wave_max(m);
@@ -101,20 +110,36 @@ topk_kernel(const float* __restrict__ logits, const float* __restrict__ bias, in
   }
 }
 
-int launch_topk(const float* logits, const float* bias, int T, int E, int k, float scaling,
-                int32_t* idx, float* gate, hipStream_t st) {
+int launch_topk(const float* partials, int nsplit, const float* col_bias, float* logits_out,
+                const float* bias, int T, int E, int k, float scaling, int32_t* idx, float* gate,
+                hipStream_t st) {
   const dim3 grid((T + 3) / 4), block(256);
+#define MOE_TOPK_ARGS partials, nsplit, col_bias, logits_out, bias, T, E, k, scaling, idx, gate
   if (E <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, st, MOE_TOPK_ARGS);
   else if (E <= 128)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, MOE_TOPK_ARGS);
   else if (E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, st, MOE_TOPK_ARGS);
   else if (E <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, MOE_TOPK_ARGS);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, logits, bias, T, E, k, scaling, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, MOE_TOPK_ARGS);
+#undef MOE_TOPK_ARGS
   return check_launch();
+}
+
+// Split the router's K loop until there are about 1024 (tile, split) work
+// items, keeping at least two K-steps per split; the split count divides the
+// K-step count.  A function of the shape only, so the workspace size is too.
+int router_ksplit(int T, int E, int d_model, int dtype) {
+  const int bk = dtype == MOE_BF16 ? 64 : 32;
+  const int nK = d_model / bk;
+  const long tiles = (long)((T + 15) / 16) * ((E + 127) / 128);
+  if ((long)(T / 128) * ((E + 127) / 128) >= 256) return 1;  // 128x128 tiles, enough of them
+  int s = 1;
+  while (tiles * s * 2 <= 1024 && nK % (s * 2) == 0 && nK / (s * 2) >= 2) s *= 2;
+  return s;
 }
 
 }  // namespace moe
