@@ -54,6 +54,23 @@ def gate_up_units(w, A, U):
     return flops, byts
 
 
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary of
+    this workload, or None when there is none or the GEMM sources changed
+    since the counters were taken."""
+    from sparse_moe_layer_03_amd import traffic as TR
+
+    summ = TR.read_summary(os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.txt"))
+    if not summ:
+        return None
+    srcs = [os.path.join(ROOT, p) for p in summ.get("sources", [])]
+    if not srcs or not all(os.path.exists(p) for p in srcs):
+        return None
+    if TR.source_hash(srcs) != summ.get("source_hash"):
+        return None
+    return float(summ["traffic_bytes"])
+
+
 def cpu_baseline(w, m, budget_s=12.0):
     """Time the oracle (as it stands) on the host cores: whole batches of the
     workload, in order, until about ``budget_s`` seconds of oracle work."""
@@ -188,7 +205,7 @@ def main():
         roof = {"bound": "hbm", "achieved": float(np.sum(by) / gu_s.sum() / 1e9),
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "grouped_gemm_kernel (gate/up + SwiGLU), mean %.4f ms/launch" % (
         gu_s.mean() * 1e3)
 

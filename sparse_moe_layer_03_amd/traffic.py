@@ -1,0 +1,127 @@
+"""HBM traffic of a kernel from rocprofv3 counters, calibrated on a copy.
+
+    python -m sparse_moe_layer_03_amd.traffic probe
+        Runs a plain device-to-device copy of COPY_BYTES (3 times; torch's
+        same-dtype copy_ is the runtime's copy kernel) so that FETCH_SIZE /
+        WRITE_SIZE can be read for a transfer of known size.
+
+    python -m sparse_moe_layer_03_amd.traffic summarize OUT.txt \\
+        --kernel-fetch K.csv --kernel-write K.csv --copy-fetch C.csv \\
+        --copy-write C.csv --kernel-regex REGEX --copy-regex REGEX \\
+        --source FILE [--source FILE ...] --command "..."
+        Reads rocprofv3 counter_collection CSVs (one counter per run) and
+        writes a text summary: per-dispatch KiB of the kernel, the copy's
+        KiB per KiB actually moved (the scale), the kernel's scaled bytes per
+        launch, and a hash of the kernel's sources (a reader of the summary
+        can tell whether the kernel changed since the counters were taken).
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import statistics
+import sys
+
+COPY_BYTES = 1 << 30
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in sorted(paths):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def probe() -> None:
+    import torch
+
+    n = COPY_BYTES // 2
+    src = torch.full((n,), 1.0, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x3", flush=True)
+
+
+def per_dispatch(path, regex, counter):
+    vals = []
+    rx = re.compile(regex)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for /{regex}/ in {path}")
+    return vals
+
+
+def summarize(a) -> None:
+    kf = per_dispatch(a.kernel_fetch, a.kernel_regex, "FETCH_SIZE")
+    kw = per_dispatch(a.kernel_write, a.kernel_regex, "WRITE_SIZE")
+    cf = per_dispatch(a.copy_fetch, a.copy_regex, "FETCH_SIZE")
+    cw = per_dispatch(a.copy_write, a.copy_regex, "WRITE_SIZE")
+    kib = COPY_BYTES / 1024.0
+    s_f = statistics.median(cf) / kib    # counter KiB per KiB really read
+    s_w = statistics.median(cw) / kib
+    fetch_b = statistics.median(kf) * 1024.0 / s_f
+    write_b = statistics.median(kw) * 1024.0 / s_w
+    lines = [
+        f"# HBM traffic per launch of /{a.kernel_regex}/ (rocprofv3 --pmc, one counter per run)",
+        f"# command: {a.command}",
+        f"kernel_fetch_kib_per_dispatch_median {statistics.median(kf):.1f}  (n={len(kf)})",
+        f"kernel_write_kib_per_dispatch_median {statistics.median(kw):.1f}  (n={len(kw)})",
+        f"copy_fetch_kib_per_dispatch_median {statistics.median(cf):.1f}  (copy of {COPY_BYTES} B)",
+        f"copy_write_kib_per_dispatch_median {statistics.median(cw):.1f}",
+        f"scale_fetch {s_f:.4f}  scale_write {s_w:.4f}  (counter KiB per KiB moved)",
+        f"traffic_fetch_bytes {fetch_b:.0f}",
+        f"traffic_write_bytes {write_b:.0f}",
+        f"traffic_bytes {fetch_b + write_b:.0f}",
+        f"source_hash {source_hash(a.source)}",
+        "sources " + " ".join(os.path.relpath(p) for p in a.source),
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_summary(path):
+    """Parse a summary written by summarize(); None if absent."""
+    if not os.path.exists(path):
+        return None
+    out = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("#") or not ln.strip():
+                continue
+            k, v = ln.split(None, 1)
+            out[k] = v.strip().split()[0] if k != "sources" else v.split()
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub.add_parser("probe")
+    s = sub.add_parser("summarize")
+    s.add_argument("out")
+    for k in ("kernel-fetch", "kernel-write", "copy-fetch", "copy-write", "kernel-regex",
+              "copy-regex", "command"):
+        s.add_argument("--" + k, required=True)
+    s.add_argument("--source", action="append", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "probe":
+        probe()
+    else:
+        summarize(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
