@@ -41,6 +41,9 @@ def parse():
                     choices=["small_bf16", "decode_bf16", "prefill_bf16", "skewed_bf16",
                              "tiny_f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--balance", type=float, default=0.0,
+                    help="per-expert load-balancing step (moe_balance_update) after the PID; "
+                         "0 = off")
     return ap.parse_args()
 
 
@@ -128,7 +131,7 @@ def main():
     bias = bias0.clone()
     lb = S.zipf_logit_offset(w, alpha, dev) if w.zipf_s else None
     wg, wu, wd = S.make_experts(w, dev)
-    n_x = min(max(args.steps, 1), 20) if w.pid else 1
+    n_x = min(max(args.steps, 1), w.batches) if w.pid else 1
     xs = [S.make_x(w, b, dev) for b in range(n_x)]
     shape = B.make_shape(w.T, w.d_model, w.n_ffn, w.n_zero, w.d_ff, w.top_k, w.dtype,
                          w.routed_scaling)
@@ -160,8 +163,14 @@ def main():
         if params is not None:
             B.moe_pid_update(shape, params, buf.counts, buf.pid_state, bias, r_log,
                              r_log.numel())
+        if args.balance > 0:
+            B.moe_balance_update(shape, args.balance, buf.counts, bias)
+        if load_log is not None:
+            load_log[i % load_log.shape[0]].copy_(buf.counts[: w.n_ffn])
         if ev is not None:
             ev[6].record(stream)
+
+    load_log = None
 
     # ---- warm-up, then restore the initial controller state
     for i in range(args.warmup):
@@ -173,6 +182,9 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    if args.balance > 0:
+        # per-step FFN loads for the load-gap report (a small device copy per step)
+        load_log = torch.zeros((K, w.n_ffn), dtype=torch.int32, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -233,6 +245,12 @@ def main():
     }
     if w.pid:
         line["r_per_step"] = [round(float(v), 4) for v in r_log.cpu().numpy()[:K]]
+    if load_log is not None:
+        ll = load_log.cpu().numpy().astype(np.float64)
+        line["balance_gamma"] = args.balance
+        line["ffn_load_max_over_mean_per_step"] = [
+            round(float(r.max() / max(r.mean(), 1e-9)), 2) for r in ll]
+        line["ffn_load_variance_per_step"] = [round(float(r.var()), 1) for r in ll]
 
     if not args.no_cpu_baseline and w.name in ("small_bf16", "skewed_bf16", "tiny_f32"):
         m = dict(wr=wr, lb=lb, bias0=bias0, wg=wg, wu=wu, wd=wd, xs=xs)

@@ -186,6 +186,20 @@ int moe_pid_update(const moe_shape* shape, const moe_pid_params* pid_params,
                    const int32_t* counts, moe_pid_state* state, float* bias,
                    float* r_log, int32_t r_log_len, void* stream);
 
+/* moe_balance_update -- per-expert load balancing on the router bias
+ * (Ascend deployment article, section "MoE专家动态负载均衡": token loads per
+ * expert vary widely and dynamic balancing narrows the gap; the method is
+ * not given -- this is a zero-sum sign step):
+ *   A = sum_{e<n_ffn} counts[e];  s_e = sign(A - n_ffn * counts[e])
+ *   S = sum_{e<n_ffn} s_e;   bias[e] += gamma * ((n_ffn * s_e - S) / n_ffn)
+ * for e < n_ffn (fp32, one rounding for the division and one for the
+ * product); identity experts untouched.  Over-loaded experts move down,
+ * under-loaded ones up, and the mean FFN bias (the PID's lever) is
+ * unchanged.  counts [E] int32 (from moe_dispatch); bias [E] fp32 in place.
+ * gamma >= 0 and finite (else MOE_EINVAL / MOE_ENONFINITE). */
+int moe_balance_update(const moe_shape* shape, float gamma, const int32_t* counts,
+                       float* bias, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

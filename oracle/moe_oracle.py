@@ -45,6 +45,10 @@ Readings where the pages are silent (each is listed in the design notes):
 * Dispatch order inside an expert is stable by assignment id a = t*k + j.
 * PID: incremental form on the FFN experts' bias, error measured in real
   (FFN) experts per token, D = 0 on the first update, no anti-windup clamp.
+* Per-expert load balancing ([AS] section "MoE专家动态负载均衡": dynamic load
+  balancing narrows the gap between experts' token loads; method not
+  stated): a zero-sum sign step on the FFN experts' correction bias, so it
+  evens the load without moving the mean FFN bias the PID controls.
 """
 
 from __future__ import annotations
@@ -66,6 +70,7 @@ __all__ = [
     "combine",
     "PidState",
     "pid_update",
+    "balance_update",
     "forward",
 ]
 
@@ -282,6 +287,27 @@ def pid_update(counts, n_ffn, T, bias, state, setpoint, kp, ki, kd):
     st.prev_err = err
     st.step += 1
     return new_bias, st, r
+
+
+def balance_update(counts, n_ffn, bias, gamma):
+    """Per-expert load-balancing step on the FFN experts' bias.
+
+    [AS] "MoE专家动态负载均衡": the token load per expert varies widely and a
+    dynamic balancing step narrows the gap.  With mean FFN load
+    L = sum_{e<N} counts[e] / N and s_e = sign(L - counts[e]) (over-loaded
+    experts get -1), every FFN expert's bias moves by
+        delta_e = gamma * (s_e - mean_{e'<N} s_e'),
+    a zero-sum step (the mean FFN bias, which sets how many real experts a
+    token activates, is unchanged).  Identity experts are untouched.
+    Returns the new bias.
+    """
+    c = np.asarray(counts, dtype=np.int64)[:n_ffn]
+    # sign(L - c_e) with L = sum(c)/N, compared exactly as sum(c) vs N*c_e
+    s = np.sign(c.sum() - n_ffn * c).astype(np.float64)
+    delta = float(gamma) * (s - s.mean())
+    new_bias = _f64(bias).copy()
+    new_bias[:n_ffn] += delta
+    return new_bias
 
 
 # --------------------------------------------------------------- forward ----

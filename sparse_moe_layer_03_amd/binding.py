@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP",
 # every entry point declared in include/moe.h
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_strerror", "moe_device_cu_count", "moe_route",
                 "moe_dispatch", "moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                "moe_combine", "moe_pid_update")
+                "moe_combine", "moe_pid_update", "moe_balance_update")
 
 
 class MoeShape(ctypes.Structure):
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_down.argtypes = [sp] + [vp] * 5
         L.moe_combine.argtypes = [sp] + [vp] * 7
         L.moe_pid_update.argtypes = [sp, ctypes.POINTER(MoePidParams), vp, vp, vp, vp, i32, vp]
+        L.moe_balance_update.argtypes = [sp, ctypes.c_float, vp, vp, vp]
         for n in ENTRY_POINTS[3:]:
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -150,6 +151,11 @@ def moe_pid_update(shape, params: MoePidParams, counts, state, bias, r_log=None,
     _check("moe_pid_update", lib().moe_pid_update(ctypes.byref(shape), ctypes.byref(params),
                                                   _p(counts), _p(state), _p(bias), _p(r_log),
                                                   int(r_log_len), _stream(stream)))
+
+
+def moe_balance_update(shape, gamma, counts, bias, stream=None):
+    _check("moe_balance_update", lib().moe_balance_update(ctypes.byref(shape), float(gamma),
+                                                          _p(counts), _p(bias), _stream(stream)))
 
 
 class LayerBuffers:

@@ -265,4 +265,15 @@ int moe_pid_update(const moe_shape* s, const moe_pid_params* pp, const int32_t* 
                     r_log, r_log ? r_log_len : 0, (hipStream_t)stream);
 }
 
+int moe_balance_update(const moe_shape* s, float gamma, const int32_t* counts, float* bias,
+                       void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!counts || !bias) return MOE_EINVAL;
+  if (!isfinite(gamma)) return MOE_ENONFINITE;
+  if (gamma < 0.f) return MOE_EINVAL;
+  if (!al4(counts) || !al4(bias)) return MOE_EALIGN;
+  return launch_balance(counts, s->n_ffn, gamma, bias, (hipStream_t)stream);
+}
+
 }  // extern "C"

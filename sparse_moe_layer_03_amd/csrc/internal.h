@@ -55,6 +55,8 @@ int launch_pid(const int32_t* counts, int n_ffn, int T, float setpoint, float kp
                float kd, moe_pid_state* state, float* bias, float* r_log, int r_log_len,
                hipStream_t st);
 
+int launch_balance(const int32_t* counts, int n_ffn, float gamma, float* bias, hipStream_t st);
+
 int device_cu_count();
 int check_launch();
 

@@ -54,3 +54,41 @@ int launch_pid(const int32_t* counts, int n_ffn, int T, float setpoint, float kp
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Per-expert load balancing on the router bias, one wave64 (LongCat-2.0
+// Ascend deployment article, section "MoE专家动态负载均衡": dynamic load
+// balancing narrows the gap between the tokens experts receive).
+// With A = sum_{e<N} counts[e] and s_e = sign(A - N * counts[e]) (+1 for an
+// under-loaded expert), every FFN expert's bias moves by
+//   delta_e = gamma * ((N * s_e - S) / N),   S = sum_e s_e,
+// a zero-sum step: the mean FFN bias, which the PID steers, is unchanged.
+// Integer sums are exact; one rounding for the division, one for the product.
+__global__ void __launch_bounds__(64)
+balance_kernel(const int32_t* __restrict__ counts, int n_ffn, float gamma,
+               float* __restrict__ bias) {
+  const int lane = threadIdx.x;
+  int a = 0;
+  for (int e = lane; e < n_ffn; e += 64) a += counts[e];
+  a = wave_sum_i(a);
+  int ssum = 0;
+  for (int e = lane; e < n_ffn; e += 64) {
+    const long d = (long)a - (long)n_ffn * counts[e];
+    ssum += (d > 0) - (d < 0);
+  }
+  ssum = wave_sum_i(ssum);
+  for (int e = lane; e < n_ffn; e += 64) {
+    const long d = (long)a - (long)n_ffn * counts[e];
+    const int s = (d > 0) - (d < 0);
+    const float frac = __fdiv_rn((float)(n_ffn * s - ssum), (float)n_ffn);
+    bias[e] = __fadd_rn(bias[e], __fmul_rn(gamma, frac));
+  }
+}
+
+int launch_balance(const int32_t* counts, int n_ffn, float gamma, float* bias, hipStream_t st) {
+  hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(64), 0, st, counts, n_ffn, gamma, bias);
+  return check_launch();
+}
+
+}  // namespace moe

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert set(names) == set(B.ENTRY_POINTS)
     L = B.lib()
     for n in names:
@@ -70,6 +70,15 @@ def test_null_and_misaligned_pointers_rejected():
     assert L.moe_expert_ffn(ctypes.byref(s), a, None, None, a, a, a, a, a, a, None) == -1
     s_bad = B.MoeShape(64, 128, 8, 4, 256, 2, 0, float("inf"))
     assert L.moe_combine(ctypes.byref(s_bad), a, a, a, a, a, a, None) == -4
+
+
+def test_balance_rejects_bad_gamma():
+    s = B.make_shape(64, 128, 8, 4, 256, 2, "f32")
+    L = B.lib()
+    a = ctypes.c_void_p(0x1000)
+    assert L.moe_balance_update(ctypes.byref(s), ctypes.c_float(float("nan")), a, a, None) == -4
+    assert L.moe_balance_update(ctypes.byref(s), ctypes.c_float(-1.0), a, a, None) == -1
+    assert L.moe_balance_update(ctypes.byref(s), ctypes.c_float(0.01), None, a, None) == -1
 
 
 def test_pid_rejects_nonfinite_params():

@@ -381,3 +381,38 @@ def test_pid_checkpoint_resume_is_bit_identical():
     np.testing.assert_array_equal(np.concatenate([rs1, rs2]), rs_a)
     np.testing.assert_array_equal(b2, b_a)
     assert (st2.integral, st2.prev_err, st2.step) == (st_a.integral, st_a.prev_err, st_a.step)
+
+
+# ------------------------------------------------------- load balancing ----
+
+def test_balance_step_is_zero_sum_and_directional():
+    N = 6
+    counts = np.array([10, 0, 3, 3, 40, 4, 99, 99], np.int64)  # last two: identity experts
+    bias = np.array([0.1, -0.2, 0.0, 0.05, 0.3, 0.0, 7.0, -7.0])
+    nb = O.balance_update(counts, N, bias, 0.01)
+    d = nb - bias
+    # mean FFN load = 60/6 = 10: expert 0 sits exactly on it (sign 0)
+    s = np.array([0, 1, 1, 1, -1, 1], np.float64)
+    np.testing.assert_allclose(d[:N], 0.01 * (s - s.mean()), rtol=0, atol=1e-15)
+    assert abs(d[:N].sum()) < 1e-15                      # zero-sum over FFN experts
+    assert d[4] < 0 and d[1] > 0                          # over-loaded down, under-loaded up
+    assert d[N] == 0 and d[N + 1] == 0                    # identity experts untouched
+    np.testing.assert_array_equal(O.balance_update(np.full(8, 5), N, bias, 0.5), bias)  # equal loads
+    np.testing.assert_array_equal(O.balance_update(counts, N, bias, 0.0), bias)
+
+
+def test_balance_evens_a_two_expert_split():
+    # two FFN experts, tokens pick the larger of (p + bias); repeated steps
+    # must move the split toward 50/50 and then hold it within one step
+    rng_ = rng(70)
+    p = rng_.uniform(0, 1, size=(400, 1))
+    scores = np.hstack([p, 1.0 - p + 0.3])           # expert 1 starts favoured
+    bias = np.zeros(2)
+    shares = []
+    for _ in range(200):
+        pick = np.argmax(scores + bias[None, :], axis=1)
+        c = np.bincount(pick, minlength=2)
+        shares.append(c[0] / 400)
+        bias = O.balance_update(c, 2, bias, 0.01)
+    assert shares[0] < 0.4
+    assert abs(np.mean(shares[-20:]) - 0.5) < 0.05
