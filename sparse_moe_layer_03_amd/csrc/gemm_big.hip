@@ -6,23 +6,31 @@
 //    a few independent accumulators (the 16x16x32 form needs many waves or
 //    accumulators per SIMD to hide its latency).  A 16-byte chunk of an
 //    operand row is the 8 bf16 one lane supplies; lanes 0-31 and 32-63 take
-//    neighbouring chunks, so a stage row of CK chunks feeds CK/2 MFMA K-steps.
+//    neighbouring chunks, so a 128-byte stage row feeds 4 MFMA K-slices.
 //  * Operand tiles move HBM -> LDS with the direct-to-LDS load
 //    (global_load_lds_dwordx4): no staging registers or ds_write.  One wave
 //    instruction fills a contiguous KiB of stage rows, so each lane fetches
 //    the chunk that the row's XOR swizzle places in its slot; the swizzle
 //    keeps the 32-row fragment reads free of bank conflicts.
-//  * NS named LDS stages (one array each, K-steps of 32 or 64) and a K loop
-//    unrolled by NS, NS-1 stages in flight: the
-//    compiler can then prove that the stage being read is not the one being
-//    filled, and no vmcnt wait separates them.  Each K-step waits (vmcnt)
-//    only for its own stage, then one s_barrier.
-//  * Balanced tile heights: an expert with m rows gets ceil(m / BM) tiles of
-//    equal height, so a tile never holds a lone remainder of a few rows.
+//  * Two rings of named LDS stages (one array each, K-steps of 64): token
+//    rows in 2 stages, weights in 3.  Token rows are re-read by every n-tile
+//    of an expert and mostly hit L2, so one step of lead hides them; the
+//    weight slice of a step usually comes from HBM and is issued two steps
+//    ahead.  2 x 32 KiB + 3 x 32 KiB fill the 160 KiB of LDS.  The K loop is
+//    unrolled by 6 (both ring positions static), so the compiler can prove
+//    that the stage being read is not one being filled and emits no vmcnt
+//    wait between them.  Each K-step waits (vmcnt) only for its own stages,
+//    then one s_barrier.
+//  * Balanced tile heights: an expert with m rows gets ceil(m / 256) tiles of
+//    equal height (a multiple of 32).  A wave runs the MFMAs of only the
+//    32-row blocks that hold rows: the K loop exists once per count of
+//    active blocks, chosen per tile, so a 160-row tile costs 5/8 of a full
+//    one.
 //  * 256 x 256 tiles over 8 waves (2 per SIMD) of 128 x 64: one wave's MFMAs
 //    run while the other waits on LDS or DMA.
-//  * Persistent grid, device-side tile list, XCD-contiguous tile order (as in
-//    gemm.hip).
+//  * Persistent grid over a tile list in the workspace (per-expert m-tile
+//    prefix and owner of every m-tile, built by big_tile_list_kernel),
+//    XCD-contiguous tile order (as in gemm.hip).
 
 #include <type_traits>
 
@@ -35,8 +43,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBigMaxGroups = 1024;
-
 // s_waitcnt with only vmcnt constrained (expcnt, lgkmcnt left at their max).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -47,104 +53,83 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
-// Swizzle of the 16-byte chunk c of tile row r inside a stage whose rows hold
-// CK chunks: 8-chunk rows XOR with (r ^ (r >> 3)) & 7, 4-chunk rows with
-// ((r >> 1) ^ (r >> 3)) & 3.  Either keeps every 8-lane group (32 banks) and
-// every 16-lane group (64 banks) of a 32-row fragment read on distinct banks.
-template <int CK>
-__device__ __forceinline__ int swz(int r, int c) {
-  if (CK == 8) return c ^ ((r ^ (r >> 3)) & 7);
-  return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+// Swizzle of the 16-byte chunk c of tile row r in a 128-byte stage row:
+// XOR with (r ^ (r >> 3)) & 7 keeps every 8-lane group (32 banks) and every
+// 16-lane group (64 banks) of a 32-row fragment read on distinct banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+// Per-expert m-tile prefix tp[0..n] (tp[0] = 0) and the expert that owns
+// each m-tile, tg[m], for tiles of kBigTileRows rows.  One block of 1024.
+__global__ void __launch_bounds__(1024)
+big_tile_list_kernel(const int32_t* __restrict__ offsets, int ngroups, int32_t* __restrict__ tp,
+                     int32_t* __restrict__ tg) {
+  __shared__ int s_tmp[1024 / 64];
+  const int gi = threadIdx.x;
+  const int mt =
+      gi < ngroups ? (offsets[gi + 1] - offsets[gi] + kBigTileRows - 1) / kBigTileRows : 0;
+  const int incl = block_inclusive_scan<1024>(mt, s_tmp);
+  if (gi < ngroups) {
+    tp[gi + 1] = incl;
+    for (int m = incl - mt; m < incl; ++m) tg[m] = gi;
+  }
+  if (gi == 0) tp[0] = 0;
 }
 
-template <int MODE, int BM, int BN, int WM, int WN, int NS, int CK, int MG>
-__global__ void __launch_bounds__(64 * WM * WN, 1)
+template <int MODE, int MG>
+__global__ void __launch_bounds__(512, 1)
 grouped_gemm_big_kernel(GemmArgs g) {
-  constexpr int NW = WM * WN, NT = 64 * NW;
-  constexpr int RB = CK * 16;                       // bytes per stage row
-  constexpr int RPK = 1024 / RB;                    // rows per KiB
-  constexpr int KS = CK * 8;                        // K elements per stage
+  constexpr int BM = kBigTileRows, BN = 256, WM = 2, WN = 4, NW = WM * WN;
+  constexpr int RB = 128;                           // bytes per stage row
+  constexpr int RPK = 1024 / RB;                    // stage rows per KiB
+  constexpr int KS = RB / 2;                        // K elements per stage
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;       // 32x32 blocks per wave
   constexpr int HN = (MODE == 1) ? BN / 2 : BN;     // output columns per tile
-  constexpr int A_KB = BM / RPK, B_KB = BN / RPK;    // KiB chunks per stage
-  static_assert(A_KB % NW == 0 && B_KB % NW == 0, "chunks per wave");
-  constexpr int A_PW = A_KB / NW, B_PW = B_KB / NW;  // DMA instructions per wave
-  constexpr int L = A_PW + B_PW;
-  static_assert(NS >= 2 && NS <= 4, "two to four stages");
-  static_assert(CK == 4 || CK == 8, "64- or 128-byte stage rows");
-  static_assert(L * (NS - 1) < 64, "vmcnt range");
+  constexpr int A_PW = BM / RPK / NW;               // DMA instructions per wave
+  constexpr int B_PW = BN / RPK / NW;
+  constexpr int NKK = KS / 16;                      // MFMA K-slices per stage
   static_assert(MODE != 1 || NB % 2 == 0, "gate/up pairing");
+  static_assert(A_PW + 2 * B_PW < 64, "vmcnt range");
 
   // One array per stage (see the header comment).
   __shared__ __attribute__((aligned(1024))) char s_a0[BM * RB];
   __shared__ __attribute__((aligned(1024))) char s_a1[BM * RB];
-  __shared__ __attribute__((aligned(1024))) char s_a2[NS >= 3 ? BM * RB : 16];
-  __shared__ __attribute__((aligned(1024))) char s_a3[NS >= 4 ? BM * RB : 16];
   __shared__ __attribute__((aligned(1024))) char s_b0[BN * RB];
   __shared__ __attribute__((aligned(1024))) char s_b1[BN * RB];
-  __shared__ __attribute__((aligned(1024))) char s_b2[NS >= 3 ? BN * RB : 16];
-  __shared__ __attribute__((aligned(1024))) char s_b3[NS >= 4 ? BN * RB : 16];
-  __shared__ int s_mt[kBigMaxGroups + 1];
-  __shared__ int s_tmp[NT / 64];
+  __shared__ __attribute__((aligned(1024))) char s_b2[BN * RB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
   const int r32 = lane & 31, kg = lane >> 5;
-  const int ngroups = g.ngroups;
 
-  // ---- per-group tile counts -> prefix sums in LDS
-  {
-    constexpr int PER = (kBigMaxGroups + NT - 1) / NT;
-    int loc[PER];
-    int run = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int gi = tid * PER + i;
-      int mt = 0;
-      if (gi < ngroups) mt = (g.offsets[gi + 1] - g.offsets[gi] + BM - 1) / BM;
-      run += mt;
-      loc[i] = run;
-    }
-    const int incl = block_inclusive_scan<NT>(run, s_tmp);
-    const int base = incl - run;
-    if (tid == 0) s_mt[0] = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int gi = tid * PER + i;
-      if (gi < ngroups) s_mt[gi + 1] = base + loc[i];
-    }
-    __syncthreads();
-  }
+  const int32_t* __restrict__ tp = g.tile_prefix;
+  const int32_t* __restrict__ tgrp = g.tile_group;
   const int ntiles = (g.N + HN - 1) / HN;
-  const long total = (long)s_mt[ngroups] * ntiles;
+  const int total = tp[g.ngroups] * ntiles;
   const int G = gridDim.x, b = blockIdx.x;
   const int vid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  const int nK = g.K / KS;  // the host guarantees nK % NS == 0
+  const int nK = g.K / KS;  // the host guarantees an even count
   const size_t row_bytes = (size_t)g.K * 2;
 
-  // DMA lane geometry: lane fills slot (lane % CK) of row (lane / CK) of a
-  // KiB and fetches the logical chunk that the swizzle of that tile row
-  // stores in the slot (the swizzle is an involution in c for a fixed row).
-  const int dma_row = lane / CK;
-  const int dma_slot = lane % CK;
+  // DMA lane geometry: lane fills slot (lane % 8) of row (lane / 8) of a KiB
+  // and fetches the logical chunk that the swizzle of that tile row stores
+  // in the slot (the swizzle is an involution in c for a fixed row).
+  const int dma_row = lane / 8;
+  const int dma_slot = lane % 8;
 
-  for (long t = vid; t < total; t += G) {
-    int lo = 0, hi = ngroups - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((long)s_mt[mid] * ntiles <= t) lo = mid; else hi = mid - 1;
-    }
-    const int grp = lo;
-    const int mt_g = s_mt[grp + 1] - s_mt[grp];
-    const long local = t - (long)s_mt[grp] * ntiles;
+  for (int t = vid; t < total; t += G) {
+    const int grp = tgrp[t / ntiles];
+    const int tp0 = tp[grp];
+    const int mt_g = tp[grp + 1] - tp0;
+    const int local = t - tp0 * ntiles;
     // Within an expert, tiles go in groups of MG m-tiles x all n-tiles (n-tile
     // major inside a group), so the tiles that run together on one XCD share
     // both their token-row slices and their weight slices in L2.
-    const int grp_m0 = (int)(local / ((long)MG * ntiles)) * MG;
+    const int grp_m0 = (local / (MG * ntiles)) * MG;
     const int mg = min(MG, mt_g - grp_m0);
-    const int in_grp = (int)(local - (long)grp_m0 * ntiles);
+    const int in_grp = local - grp_m0 * ntiles;
     const int nt = in_grp / mg, mi = grp_m0 + in_grp % mg;
     const int row0 = g.offsets[grp];
     const int cnt = g.offsets[grp + 1] - row0;
@@ -152,6 +137,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int m0 = mi * h;
     const int m_end = min(cnt, m0 + h);                  // rows [m0, m_end)
     const int n0 = nt * HN;
+    // 32-row blocks of this wave that hold rows: i with (i*WM + wm)*32 < rows
+    const int nrb = (m_end - m0 + 31) / 32;
+    const int mba = min(MB, (nrb - wm + WM - 1) / WM);
 
     // ---- per-lane DMA source offsets (32-bit; bases are wave-uniform)
     const char* a_base = (const char*)g.a;
@@ -168,7 +156,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       } else {
         src_row = row0 + rr;
       }
-      a_off[q] = (uint32_t)(src_row * row_bytes) + swz<CK>(r, dma_slot) * 16;
+      a_off[q] = (uint32_t)(src_row * row_bytes) + swz(r, dma_slot) * 16;
     }
     const char* b_base0 = (const char*)g.b0 + (size_t)grp * g.N * row_bytes;
     const char* b_base1 =
@@ -179,7 +167,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       const int r = (wave + q * NW) * RPK + dma_row;
       int n = (MODE == 1 && r >= HN) ? n0 + r - HN : n0 + r;
       if (n > g.N - 1) n = g.N - 1;
-      b_off[q] = (uint32_t)(n * row_bytes) + swz<CK>(r, dma_slot) * 16;
+      b_off[q] = (uint32_t)(n * row_bytes) + swz(r, dma_slot) * 16;
     }
 
     f32x16_t acc[MB][NB];
@@ -188,36 +176,39 @@ grouped_gemm_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
 
-    auto stage_a = [&](auto bufc) -> char* {
-      constexpr int BUF = decltype(bufc)::value;
-      return BUF == 0 ? s_a0 : (BUF == 1 ? s_a1 : (BUF == 2 ? s_a2 : s_a3));
+    auto stage_a = [&](auto sc) -> char* {
+      constexpr int S = decltype(sc)::value;
+      return S == 0 ? s_a0 : s_a1;
     };
-    auto stage_b = [&](auto bufc) -> char* {
-      constexpr int BUF = decltype(bufc)::value;
-      return BUF == 0 ? s_b0 : (BUF == 1 ? s_b1 : (BUF == 2 ? s_b2 : s_b3));
+    auto stage_b = [&](auto sc) -> char* {
+      constexpr int S = decltype(sc)::value;
+      return S == 0 ? s_b0 : (S == 1 ? s_b1 : s_b2);
     };
 
-    // every stage issues exactly L loads per wave (the vmcnt waits count on
-    // it); rows past the tile were clamped to its last row above
-    auto issue = [&](auto bufc, int ks) {
-      char* sa = stage_a(bufc);
-      char* sb = stage_b(bufc);
+    // Every stage issues exactly A_PW (token rows) or B_PW (weights) loads
+    // per wave, whatever the tile height (the vmcnt waits count on it); rows
+    // past the tile were clamped to its last row above.
+    auto issue_a = [&](auto sc, int ks) {
+      char* sa = stage_a(sc);
       const size_t off = (size_t)ks * RB;
 #pragma unroll
-      for (int q = 0; q < A_PW; ++q) {
-        const int kb = wave + q * NW;
+      for (int q = 0; q < A_PW; ++q)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
-                                         (lds_void_t*)(sa + kb * 1024), 16, 0, 0);
-      }
+                                         (lds_void_t*)(sa + (wave + q * NW) * 1024), 16, 0, 0);
+    };
+    auto issue_b = [&](auto sc, int ks) {
+      char* sb = stage_b(sc);
+      const size_t off = (size_t)ks * RB;
 #pragma unroll
       for (int q = 0; q < B_PW; ++q) {
-        const int kb = wave + q * NW;
         // gate rows fill the first half of the B tile, up rows the second
-        const char* bb = (MODE == 1 && kb * RPK >= HN) ? b_base1 : b_base0;
+        // (wave < NW, so the half is fixed per q)
+        const char* bb = (MODE == 1 && (q * NW) * RPK >= HN) ? b_base1 : b_base0;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
-                                         (lds_void_t*)(sb + kb * 1024), 16, 0, 0);
+                                         (lds_void_t*)(sb + (wave + q * NW) * 1024), 16, 0, 0);
       }
     };
+    static_assert(MODE != 1 || (HN % (NW * RPK) == 0), "gate/up halves align with q");
 
     auto brow = [&](int j) {
       if (MODE == 1)
@@ -226,45 +217,57 @@ grouped_gemm_big_kernel(GemmArgs g) {
       return wn * WTN + j * 32 + r32;
     };
 
-    // One K-step of 64: wait for this stage's DMA (newer stages may stay in
-    // flight), barrier, start the DMA NS-1 steps ahead into the stage freed
-    // by the previous step, then 4 MFMA K-slices of 16 with the fragments of
-    // slice kk+1 read from LDS while slice kk computes.
-    auto kstep = [&](auto bufc, int ks) {
-      constexpr int BUF = decltype(bufc)::value;
-      const char* sa = stage_a(bufc);
-      const char* sb = stage_b(bufc);
-      // stages newer than this one that may still be in flight
-      const int ahead = min(NS - 2, nK - 1 - ks);
-      if (NS >= 4 && ahead >= 2) wait_vmcnt<(NS >= 4 ? 2 * L : 0)>();
-      else if (NS >= 3 && ahead >= 1) wait_vmcnt<(NS >= 3 ? L : 0)>();
+    // One K-step of 64 on token-row stage AS and weight stage BS, with MBA
+    // active 32-row blocks: wait for this step's stages (the weight stage of
+    // the next step may stay in flight), barrier, refill the stages the
+    // previous step read (token rows one step ahead, weights two), then 4
+    // MFMA K-slices of 16 with the fragments of slice kk+1 read from LDS
+    // while slice kk computes.  nac / nbc: whether the step issues the token
+    // rows of step ks+1 / the weights of step ks+2.  In the main loop they
+    // are compile-time true, so the compiler knows exactly which DMA is still
+    // in flight and adds no wait of its own.
+    auto kstep = [&](auto mbac, auto asc, auto bsc, auto nac, auto nbc, int ks) {
+      constexpr int MBA = decltype(mbac)::value;
+      constexpr int AS = decltype(asc)::value, BS = decltype(bsc)::value;
+      const bool next_a = nac, next_b = nbc;
+      const char* sa = stage_a(asc);
+      const char* sb = stage_b(bsc);
+      // the weights of step ks+1 were issued by the previous step iff this
+      // step issues the token rows of step ks+1
+      if (next_a) wait_vmcnt<B_PW>();
       else wait_vmcnt<0>();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      if (ks + NS - 1 < nK) issue(std::integral_constant<int, (BUF + NS - 1) % NS>{}, ks + NS - 1);
+      // Keep the DMA lane offsets 32-bit: left alone, the compiler hoists
+      // their 64-bit extensions out of the K loop, doubling their registers.
+#pragma unroll
+      for (int q = 0; q < A_PW; ++q) asm volatile("" : "+v"(a_off[q]));
+#pragma unroll
+      for (int q = 0; q < B_PW; ++q) asm volatile("" : "+v"(b_off[q]));
+      if (next_a) issue_a(std::integral_constant<int, (AS + 1) % 2>{}, ks + 1);
+      if (next_b) issue_b(std::integral_constant<int, (BS + 2) % 3>{}, ks + 2);
       // favour this wave's MFMA issue over the other wave on the SIMD
       __builtin_amdgcn_s_setprio(1);
-      u32x4_t af[2][MB], bfr[2][NB];
+      u32x4_t af[2][MBA], bfr[2][NB];
       auto load = [&](int set, int kk) {
         const int c = kk * 2 + kg;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
+        for (int i = 0; i < MBA; ++i) {
           const int r = (i * WM + wm) * 32 + r32;
-          af[set][i] = *reinterpret_cast<const u32x4_t*>(&sa[r * RB + (swz<CK>(r, c) << 4)]);
+          af[set][i] = *reinterpret_cast<const u32x4_t*>(&sa[r * RB + (swz(r, c) << 4)]);
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int r = brow(j);
-          bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * RB + (swz<CK>(r, c) << 4)]);
+          bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * RB + (swz(r, c) << 4)]);
         }
       };
-      constexpr int NKK = CK / 2;  // MFMA K-slices of 16 per stage
       load(0, 0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         if (kk + 1 < NKK) load((kk + 1) & 1, kk + 1);
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MBA; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -275,41 +278,79 @@ grouped_gemm_big_kernel(GemmArgs g) {
       // first use and stalls on it): the first slice's reads, then each
       // slice's MFMAs with the next slice's reads interleaved 1:1 at the
       // front, so they have landed before that slice starts.
-      constexpr int NR = MB + NB;        // LDS reads per slice
-      constexpr int NM = MB * NB;        // MFMAs per slice
-      static_assert(NM >= NR, "read/MFMA interleave");
+      constexpr int NR = MBA + NB;       // LDS reads per slice
+      constexpr int NM = MBA * NB;       // MFMAs per slice
+      constexpr int NP = NR < NM ? NR : NM;
       __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
       for (int kk = 0; kk + 1 < NKK; ++kk) {
 #pragma unroll
-        for (int q = 0; q < NR; ++q) {
+        for (int q = 0; q < NP; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+        if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
       __builtin_amdgcn_s_setprio(0);
     };
 
-    // previous tile's epilogue stores and LDS reads must be done before the
-    // stage buffers are refilled and before vmcnt counts only this tile's DMA
-    wait_vmcnt<0>();
-    wait_lgkm0();
-    __builtin_amdgcn_s_barrier();
-    issue(std::integral_constant<int, 0>{}, 0);
-    if (NS >= 3 && nK > 1) issue(std::integral_constant<int, 1>{}, 1);
-    if (NS >= 4 && nK > 2) issue(std::integral_constant<int, 2>{}, 2);
-    for (int ks = 0; ks < nK; ks += NS) {
-      kstep(std::integral_constant<int, 0>{}, ks);
-      kstep(std::integral_constant<int, 1>{}, ks + 1);
-      if (NS >= 3) kstep(std::integral_constant<int, (NS >= 3 ? 2 : 0)>{}, ks + 2);
-      if (NS >= 4) kstep(std::integral_constant<int, (NS >= 4 ? 3 : 0)>{}, ks + 3);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using T = std::true_type;
+    // The K loop for MBA active blocks up to the tail: both ring positions
+    // repeat every 6 steps, and the loop runs while every step in it has both
+    // refills to issue (ks + 8 <= nK); K is a multiple of 128, so 2, 4 or 6
+    // steps remain for the tail.  Returns the first tail step.
+    auto kloop = [&](auto mbac) {
+      // previous tile's epilogue stores and LDS reads must be done before the
+      // stages are refilled and before vmcnt counts only this tile's DMA
+      wait_vmcnt<0>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      issue_a(I0{}, 0);
+      issue_b(I0{}, 0);
+      issue_b(I1{}, 1);  // nK >= 2
+      int ks = 0;
+      for (; ks + 8 <= nK; ks += 6) {
+        kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
+        kstep(mbac, I1{}, I1{}, T{}, T{}, ks + 1);
+        kstep(mbac, I0{}, I2{}, T{}, T{}, ks + 2);
+        kstep(mbac, I1{}, I0{}, T{}, T{}, ks + 3);
+        kstep(mbac, I0{}, I1{}, T{}, T{}, ks + 4);
+        kstep(mbac, I1{}, I2{}, T{}, T{}, ks + 5);
+      }
+      return ks;
+    };
+    // a wave with no rows (mba == 0) still loads and waits with the others;
+    // its one block of clamped rows is never stored
+    int ks;
+    if (mba >= 4) ks = kloop(std::integral_constant<int, 4>{});
+    else if (mba == 3) ks = kloop(std::integral_constant<int, 3>{});
+    else if (mba == 2) ks = kloop(std::integral_constant<int, 2>{});
+    else ks = kloop(std::integral_constant<int, 1>{});
+    // The last 2, 4 or 6 steps run every block (one copy of the code; blocks
+    // without rows are never stored) with refills decided at run time.
+    {
+      using M4 = std::integral_constant<int, 4>;
+      kstep(M4{}, I0{}, I0{}, ks + 1 < nK, ks + 2 < nK, ks);
+      kstep(M4{}, I1{}, I1{}, ks + 2 < nK, ks + 3 < nK, ks + 1);
+      if (ks + 4 <= nK) {
+        kstep(M4{}, I0{}, I2{}, ks + 3 < nK, ks + 4 < nK, ks + 2);
+        kstep(M4{}, I1{}, I0{}, ks + 4 < nK, ks + 5 < nK, ks + 3);
+      }
+      if (ks + 6 <= nK) {
+        kstep(M4{}, I0{}, I1{}, ks + 5 < nK, ks + 6 < nK, ks + 4);
+        kstep(M4{}, I1{}, I2{}, false, false, ks + 5);
+      }
     }
 
     // ---- epilogue.  Weights were the MFMA row operand, so block (i, j) is
     // C^T: lane (r32, kg) holds, for quad q = v / 4, the 4 consecutive output
     // columns 8q + 4kg + {0..3} of token row r32 -> one packed 8-byte store.
+    // Blocks past the wave's active ones hold rows >= m_end and are skipped.
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int r = m0 + (i * WM + wm) * 32 + r32;
@@ -357,30 +398,32 @@ grouped_gemm_big_kernel(GemmArgs g) {
   }
 }
 
-#ifndef MOE_HUGE_TILE
-#define MOE_HUGE_TILE 256, 256, 2, 4, 2, 8, 4
+#ifndef MOE_BIG_MG
+#define MOE_BIG_MG 4
 #endif
-
-template <int BM, int BN, int WM, int WN, int NS, int CK, int MG>
-struct BigCfg {
-  static constexpr int KSTEP_MULT = NS * CK * 8;  // K must be a multiple of this
-  static constexpr int NT = 64 * WM * WN;
-};
 
 template <int MODE>
 static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
-  auto kern = grouped_gemm_big_kernel<MODE, MOE_HUGE_TILE>;
+  auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG>;
   const int cus = device_cu_count();
   if (cus <= 0) return MOE_EHIP;
   int grid = cus;  // one workgroup per CU (LDS bound)
   grid -= grid % 8;
   if (grid < 8) grid = 8;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(BigCfg<MOE_HUGE_TILE>::NT), 0, st, g);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, st, g);
   return check_launch();
 }
 
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
+  if (g.tile_prefix == nullptr || g.tile_group == nullptr || g.K % 128 != 0) return MOE_EINVAL;
   return mode == 1 ? launch_big_mode<1>(g, st) : launch_big_mode<2>(g, st);
+}
+
+int launch_big_tile_list(const int32_t* offsets, int ngroups, int32_t* tp, int32_t* tg,
+                         hipStream_t st) {
+  if (ngroups < 1 || ngroups > 1024) return MOE_EINVAL;
+  hipLaunchKernelGGL(big_tile_list_kernel, dim3(1), dim3(1024), 0, st, offsets, ngroups, tp, tg);
+  return check_launch();
 }
 
 }  // namespace moe
