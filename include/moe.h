@@ -159,9 +159,7 @@ int moe_ffn_gate_up(const moe_shape* shape, const void* x, const void* x_perm,
                     void* stream);
 
 /* moe_ffn_down -- second half of moe_expert_ffn: y_perm rows = H Wd^T, with
- * H (and, for many rows per expert, the expert tile list) read from the
- * workspace written by the preceding moe_ffn_gate_up with the same shape and
- * offsets. */
+ * H read from the workspace written by moe_ffn_gate_up. */
 int moe_ffn_down(const moe_shape* shape, const int32_t* offsets,
                  const void* w_down, void* y_perm, void* ws, void* stream);
 

@@ -7,6 +7,8 @@
 
 #include <atomic>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -60,7 +62,7 @@ static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 struct WsLayout {
-  size_t logits, hist, h, tiles, total;
+  size_t logits, hist, h, total;
 };
 
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -77,9 +79,6 @@ static WsLayout ws_layout(const moe_shape* s) {
   off = up256(off + E * (size_t)dispatch_blocks((long)Tk) * sizeof(int32_t));
   w.h = off;
   off = up256(off + Tk * (size_t)s->d_ff * elem_size(s->dtype));
-  w.tiles = off;  // tile list of the many-row expert GEMMs: prefix, then owners
-  off = up256(off + ((size_t)s->n_ffn + 1 + big_tile_list_max((long)Tk, s->n_ffn)) *
-                        sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -96,9 +95,16 @@ static int ffn_big_tiles(const moe_shape* s) {
 // may come from x_perm, which has T*k rows).
 static bool ffn_use_big(const moe_shape* s) {
   const size_t Tk = (size_t)s->T * s->top_k;
-  return ffn_big_tiles(s) && s->dtype == MOE_BF16 && s->d_model % 128 == 0 &&
-         s->d_ff % 128 == 0 && Tk * s->d_model * 2 < (1ull << 32) &&
-         Tk * s->d_ff * 2 < (1ull << 32) && (size_t)s->d_ff * s->d_model * 2 < (1ull << 32);
+  if (!(ffn_big_tiles(s) && s->dtype == MOE_BF16 && s->d_model % 128 == 0 &&
+        s->d_ff % 128 == 0 && Tk * s->d_model * 2 < (1ull << 32) &&
+        Tk * s->d_ff * 2 < (1ull << 32) && (size_t)s->d_ff * s->d_model * 2 < (1ull << 32)))
+    return false;
+  // each workgroup tracks at most 128 tiles (gate/up: d_ff/128 column
+  // tiles per m-tile, down: d_model/256); the m-tile count of the first
+  // group is packed into 22 bits
+  const long mt = big_tile_list_max((long)Tk, s->n_ffn);
+  const long nt = std::max((long)s->d_ff / 128, (long)s->d_model / 256);
+  return mt < (1l << 22) && mt * nt <= 128l * big_grid();
 }
 
 // 128x128 router tiles when there are enough of them (prefill), else 16-row
@@ -206,16 +212,7 @@ int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
   g.ksplit = 1;
-  if (ffn_use_big(s)) {
-    const WsLayout w = ws_layout(s);
-    int32_t* tp = (int32_t*)((char*)ws + w.tiles);
-    int32_t* tg = tp + s->n_ffn + 1;
-    rc = launch_big_tile_list(offsets, s->n_ffn, tp, tg, (hipStream_t)stream);
-    if (rc) return rc;
-    g.tile_prefix = tp;
-    g.tile_group = tg;
-    return launch_gemm_big(1, g, (hipStream_t)stream);
-  }
+  if (ffn_use_big(s)) return launch_gemm_big(1, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 
@@ -236,13 +233,7 @@ int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down,
   g.top_k = s->top_k;
   g.M = s->T;
   g.ksplit = 1;
-  if (ffn_use_big(s)) {
-    // the tile list written by moe_ffn_gate_up for the same offsets
-    const int32_t* tp = (const int32_t*)((char*)ws + ws_layout(s).tiles);
-    g.tile_prefix = tp;
-    g.tile_group = tp + s->n_ffn + 1;
-    return launch_gemm_big(2, g, (hipStream_t)stream);
-  }
+  if (ffn_use_big(s)) return launch_gemm_big(2, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 

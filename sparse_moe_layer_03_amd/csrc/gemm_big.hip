@@ -28,9 +28,8 @@
 //    one.
 //  * 256 x 256 tiles over 8 waves (2 per SIMD) of 128 x 64: one wave's MFMAs
 //    run while the other waits on LDS or DMA.
-//  * Persistent grid over a tile list in the workspace (per-expert m-tile
-//    prefix and owner of every m-tile, built by big_tile_list_kernel),
-//    XCD-contiguous tile order (as in gemm.hip).
+//  * Persistent grid, XCD-contiguous tile order (as in gemm.hip); each
+//    workgroup finds the experts of its own tiles at the start.
 
 #include <type_traits>
 
@@ -58,27 +57,12 @@ __device__ __forceinline__ void wait_lgkm0() {
 // 16-lane group (64 banks) of a 32-row fragment read on distinct banks.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
-// Per-expert m-tile prefix tp[0..n] (tp[0] = 0) and the expert that owns
-// each m-tile, tg[m], for tiles of kBigTileRows rows.  One block of 1024.
-__global__ void __launch_bounds__(1024)
-big_tile_list_kernel(const int32_t* __restrict__ offsets, int ngroups, int32_t* __restrict__ tp,
-                     int32_t* __restrict__ tg) {
-  __shared__ int s_tmp[1024 / 64];
-  const int gi = threadIdx.x;
-  const int mt =
-      gi < ngroups ? (offsets[gi + 1] - offsets[gi] + kBigTileRows - 1) / kBigTileRows : 0;
-  const int incl = block_inclusive_scan<1024>(mt, s_tmp);
-  if (gi < ngroups) {
-    tp[gi + 1] = incl;
-    for (int m = incl - mt; m < incl; ++m) tg[m] = gi;
-  }
-  if (gi == 0) tp[0] = 0;
-}
+constexpr int kBigMaxGroups = 1024;
 
 template <int MODE, int MG>
 __global__ void __launch_bounds__(512, 1)
 grouped_gemm_big_kernel(GemmArgs g) {
-  constexpr int BM = kBigTileRows, BN = 256, WM = 2, WN = 4, NW = WM * WN;
+  constexpr int BM = kBigTileRows, BN = 256, WM = 2, WN = 4, NW = WM * WN, NT = 64 * NW;
   constexpr int RB = 128;                           // bytes per stage row
   constexpr int RPK = 1024 / RB;                    // stage rows per KiB
   constexpr int KS = RB / 2;                        // K elements per stage
@@ -104,12 +88,55 @@ grouped_gemm_big_kernel(GemmArgs g) {
   const int wm = wave / WN, wn = wave % WN;
   const int r32 = lane & 31, kg = lane >> 5;
 
-  const int32_t* __restrict__ tp = g.tile_prefix;
-  const int32_t* __restrict__ tgrp = g.tile_group;
+  const int ngroups = g.ngroups;
   const int ntiles = (g.N + HN - 1) / HN;
-  const int total = tp[g.ngroups] * ntiles;
   const int G = gridDim.x, b = blockIdx.x;
   const int vid = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+
+  // ---- this workgroup's tiles.  The per-group m-tile prefix is built in the
+  // first token-row stage (no DMA has started yet); lane l of every wave then
+  // looks up the group of tiles vid + l*G and vid + (64 + l)*G and keeps it,
+  // packed with the group's first m-tile, in one register each (the host
+  // guarantees at most 128 tiles per workgroup); the tile loop reads them
+  // back with readlane.
+  int* s_pref = reinterpret_cast<int*>(s_a0);  // ngroups + 1 <= 1025 ints
+  int* s_scan = reinterpret_cast<int*>(s_a1);  // NT / 64 ints
+  {
+    constexpr int PER = (kBigMaxGroups + NT - 1) / NT;
+    int loc[PER];
+    int run = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int gi = tid * PER + i;
+      int mt = 0;
+      if (gi < ngroups) mt = (g.offsets[gi + 1] - g.offsets[gi] + BM - 1) / BM;
+      run += mt;
+      loc[i] = run;
+    }
+    const int incl = block_inclusive_scan<NT>(run, s_scan);
+    const int base = incl - run;
+    if (tid == 0) s_pref[0] = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int gi = tid * PER + i;
+      if (gi < ngroups) s_pref[gi + 1] = base + loc[i];
+    }
+    __syncthreads();
+  }
+  const int total = s_pref[ngroups] * ntiles;
+  auto find = [&](int t) -> uint32_t {  // (first m-tile << 10) | group
+    if (t >= total) return 0;
+    const int m = t / ntiles;
+    int lo = 0, hi = ngroups - 1;  // last group with s_pref[grp] <= m
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pref[mid] <= m) lo = mid; else hi = mid - 1;
+    }
+    return ((uint32_t)s_pref[lo] << 10) | (uint32_t)lo;
+  };
+  const uint32_t tdesc0 = find(vid + lane * G);
+  const uint32_t tdesc1 = find(vid + (64 + lane) * G);
+  __syncthreads();  // the prefix is dead before the first DMA into s_a0
   const int nK = g.K / KS;  // the host guarantees an even count
   const size_t row_bytes = (size_t)g.K * 2;
 
@@ -119,10 +146,14 @@ grouped_gemm_big_kernel(GemmArgs g) {
   const int dma_row = lane / 8;
   const int dma_slot = lane % 8;
 
-  for (int t = vid; t < total; t += G) {
-    const int grp = tgrp[t / ntiles];
-    const int tp0 = tp[grp];
-    const int mt_g = tp[grp + 1] - tp0;
+  for (int k = 0; vid + k * G < total; ++k) {
+    const int t = vid + k * G;
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(
+        (int)(k < 64 ? tdesc0 : tdesc1), k & 63);
+    const int grp = (int)(d & 1023u);
+    const int tp0 = (int)(d >> 10);
+    const int cnt_g = g.offsets[grp + 1] - g.offsets[grp];
+    const int mt_g = (cnt_g + BM - 1) / BM;
     const int local = t - tp0 * ntiles;
     // Within an expert, tiles go in groups of MG m-tiles x all n-tiles (n-tile
     // major inside a group), so the tiles that run together on one XCD share
@@ -402,28 +433,23 @@ grouped_gemm_big_kernel(GemmArgs g) {
 #define MOE_BIG_MG 4
 #endif
 
+int big_grid() {
+  int grid = device_cu_count();  // one workgroup per CU (LDS bound)
+  grid -= grid % 8;
+  return grid < 8 ? 8 : grid;
+}
+
 template <int MODE>
 static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
   auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG>;
-  const int cus = device_cu_count();
-  if (cus <= 0) return MOE_EHIP;
-  int grid = cus;  // one workgroup per CU (LDS bound)
-  grid -= grid % 8;
-  if (grid < 8) grid = 8;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, st, g);
+  if (device_cu_count() <= 0) return MOE_EHIP;
+  hipLaunchKernelGGL(kern, dim3(big_grid()), dim3(512), 0, st, g);
   return check_launch();
 }
 
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
-  if (g.tile_prefix == nullptr || g.tile_group == nullptr || g.K % 128 != 0) return MOE_EINVAL;
+  if (g.K % 128 != 0 || g.ngroups < 1 || g.ngroups > kBigMaxGroups) return MOE_EINVAL;
   return mode == 1 ? launch_big_mode<1>(g, st) : launch_big_mode<2>(g, st);
-}
-
-int launch_big_tile_list(const int32_t* offsets, int ngroups, int32_t* tp, int32_t* tg,
-                         hipStream_t st) {
-  if (ngroups < 1 || ngroups > 1024) return MOE_EINVAL;
-  hipLaunchKernelGGL(big_tile_list_kernel, dim3(1), dim3(1024), 0, st, offsets, ngroups, tp, tg);
-  return check_launch();
 }
 
 }  // namespace moe

@@ -22,8 +22,6 @@ struct GemmArgs {
   int ngroups;             // experts (grouped modes)
   int top_k;
   int ksplit;              // router: K is split into this many partial sums
-  const int32_t* tile_prefix;  // big kernel: per-group m-tile prefix [ngroups + 1]
-  const int32_t* tile_group;   // big kernel: owning group of every m-tile
 };
 
 // mode: 0 router, 1 gate/up + SwiGLU, 2 down.  big: 128x128 tiles, else
@@ -31,14 +29,11 @@ struct GemmArgs {
 int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st);
 
 // bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles
-// over the tile list written by launch_big_tile_list (K a multiple of 128).
+// (K a multiple of 128, at most 1024 groups, at most 128 tiles per
+// workgroup of the big_grid() launched).
 constexpr int kBigTileRows = 256;
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st);
-
-// Tile list of the big kernel from group row offsets: tp [ngroups + 1] and
-// tg [big_tile_list_max(...)] int32.
-int launch_big_tile_list(const int32_t* offsets, int ngroups, int32_t* tp, int32_t* tg,
-                         hipStream_t st);
+int big_grid();
 
 // Upper bound on the m-tiles of ngroups groups holding rows rows in total.
 inline long big_tile_list_max(long rows, int ngroups) {
