@@ -1,19 +1,32 @@
 """Summarise a rocprofv3 results database (rocpd SQLite) per kernel:
 calls, total/average/min/max duration.  Reads only the database file.
 
-    python -m sparse_moe_layer_03_amd.rocpd_stats path/to/results.db [name-substring]
+    python -m sparse_moe_layer_03_amd.rocpd_stats path/to/results.db [--skip N] [name-substring]
+
+--skip N leaves out the first N calls of every kernel (in start order), e.g.
+the warm-up steps of a bench run, so that the averages cover the timed steps.
 """
 import sqlite3
 import sys
 
 
-def main(path, filt=None):
+def main(path, filt=None, skip=0):
     cur = sqlite3.connect(path).cursor()
-    rows = cur.execute(
-        "select name, count(*), sum(duration), avg(duration), min(duration), max(duration), "
-        "max(grid_x), max(workgroup_x), max(vgpr_count), max(accum_vgpr_count), max(lds_size) "
-        "from kernels group by name order by sum(duration) desc").fetchall()
-    tot = sum(r[2] for r in rows)
+    data = {}
+    for name, start, dur, gx, wx, v, ag, lds in cur.execute(
+            "select name, start, duration, grid_x, workgroup_x, vgpr_count, accum_vgpr_count, "
+            "lds_size from kernels order by start"):
+        d = data.setdefault(name, {"durs": [], "meta": (gx, wx, v, ag, lds)})
+        d["durs"].append(dur)
+    rows = []
+    for name, d in data.items():
+        durs = d["durs"][skip:]
+        if not durs:
+            continue
+        rows.append((name, len(durs), sum(durs), sum(durs) / len(durs), min(durs), max(durs),
+                     *d["meta"]))
+    rows.sort(key=lambda r: -r[2])
+    tot = sum(r[2] for r in rows) or 1
     print(f"{'kernel':<70} {'calls':>6} {'total_us':>10} {'avg_us':>9} {'min_us':>9} "
           f"{'max_us':>9} {'pct':>6}  grid wg vgpr agpr lds")
     for n, c, s, a, mn, mx, gx, wx, v, ag, lds in rows:
@@ -24,4 +37,10 @@ def main(path, filt=None):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1], sys.argv[2] if len(sys.argv) > 2 else None)
+    args = sys.argv[1:]
+    skip = 0
+    if "--skip" in args:
+        i = args.index("--skip")
+        skip = int(args[i + 1])
+        del args[i:i + 2]
+    main(args[0], args[1] if len(args) > 1 else None, skip)
