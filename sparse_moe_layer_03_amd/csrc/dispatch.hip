@@ -6,11 +6,14 @@
 //
 //   hist    nb blocks: block b counts its contiguous chunk of assignments
 //           into LDS and writes the expert-major table hist[e * nb + b].
-//   scan    one block: exclusive scan of that table -> the first sorted
-//           position of (expert e, chunk b); counts and offsets.
-//   scatter nb blocks: each of the 4 waves of block b owns a quarter of the
-//           chunk; wave-level histograms give each wave its starting
-//           position per expert, then the wave walks its quarter 64
+//   rows    one wave per expert: exclusive scan of the expert's row of that
+//           table (contiguous, so the reads coalesce) -> the first position
+//           of chunk b inside expert e's segment; the row total is counts[e].
+//   scatter nb blocks: each block scans counts into the expert offsets (block
+//           0 writes them out), so (expert e, chunk b) starts at
+//           offsets[e] + row prefix.  Each of the 4 waves of block b owns a
+//           quarter of the chunk; wave-level histograms give each wave its
+//           starting position per expert, then the wave walks its quarter 64
 //           assignments at a time, ranking equal experts among the lanes
 //           with a ballot-built peer mask.
 
@@ -37,41 +40,70 @@ dispatch_hist_kernel(const int32_t* __restrict__ idx, int Tk, int E, int32_t* __
   for (int e = threadIdx.x; e < E; e += kDispThreads) hist[(size_t)e * nb + b] = s_h[e];
 }
 
-// Single block of 1024 threads; each thread scans a contiguous segment.
-__global__ void __launch_bounds__(1024)
-dispatch_scan_kernel(int32_t* __restrict__ hist, int nb, int E, int Tk,
-                     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  __shared__ int s_tmp[1024 / 64];
-  const int n = E * nb;
-  const int per = (n + 1023) / 1024;
-  const int lo = threadIdx.x * per, hi = min(n, lo + per);
+// One wave per expert e: exclusive prefix of hist[e * nb + 0 .. nb) over the
+// chunks (nb <= 256, 4 per lane), written back in place; counts[e] = total.
+__global__ void __launch_bounds__(kDispThreads)
+dispatch_rows_kernel(int32_t* __restrict__ hist, int nb, int E, int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * (kDispThreads / 64) + (threadIdx.x >> 6);
+  if (e >= E) return;  // uniform per wave
+  const int lane = lane_id();
+  int32_t* row = hist + (size_t)e * nb;
+  int v[4];
   int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += hist[i];
-  // counts per expert (independent of the scan)
-  const int incl = block_inclusive_scan<1024>(sum, s_tmp);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // lane holds chunks 4*lane .. 4*lane+3
+    const int c = lane * 4 + i;
+    v[i] = c < nb ? row[c] : 0;
+    sum += v[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += u;
+  }
   int run = incl - sum;
-  for (int i = lo; i < hi; ++i) {
-    const int v = hist[i];
-    hist[i] = run;  // becomes the start position of (e, b)
-    run += v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = lane * 4 + i;
+    if (c < nb) row[c] = run;
+    run += v[i];
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    const int start = hist[(size_t)e * nb];
-    const int end = (e + 1 < E) ? hist[(size_t)(e + 1) * nb] : Tk;
-    offsets[e] = start;
-    counts[e] = end - start;
-  }
-  if (threadIdx.x == 0) offsets[E] = Tk;
+  if (lane == 63) counts[e] = incl;
 }
 
 template <int NBITS>
 __global__ void __launch_bounds__(kDispThreads)
 dispatch_scatter_kernel(const int32_t* __restrict__ idx, int Tk, int E,
-                        const int32_t* __restrict__ base, int32_t* __restrict__ perm,
+                        const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
+                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                         int32_t* __restrict__ inv_perm) {
-  extern __shared__ int s_w[];  // [4][E]
+  extern __shared__ int s_w[];  // [4][E] wave cursors, then [E] expert offsets
+  __shared__ int s_tmp[kDispThreads / 64];
+  int* s_off = s_w + 4 * E;
   const int nb = gridDim.x, b = blockIdx.x;
+  {
+    // expert offsets: exclusive scan of counts (E <= 1024, 4 per thread)
+    int c[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x * 4 + i;
+      c[i] = e < E ? counts[e] : 0;
+      sum += c[i];
+    }
+    int run = block_inclusive_scan<kDispThreads>(sum, s_tmp) - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x * 4 + i;
+      if (e < E) {
+        s_off[e] = run;
+        if (b == 0) offsets[e] = run;
+      }
+      run += c[i];
+    }
+    if (b == 0 && threadIdx.x == 0) offsets[E] = Tk;
+  }
   const int chunk = (Tk + nb - 1) / nb;
   const int lo = b * chunk, hi = min(Tk, lo + chunk);
   const int w = threadIdx.x >> 6, lane = lane_id();
@@ -86,7 +118,7 @@ dispatch_scatter_kernel(const int32_t* __restrict__ idx, int Tk, int E,
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kDispThreads) {
-    int run = base[(size_t)e * nb + b];
+    int run = s_off[e] + base[(size_t)e * nb + b];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = s_w[q * E + e];
@@ -129,17 +161,17 @@ int launch_dispatch(const int32_t* idx, int Tk, int E, int nb, int32_t* block_hi
                      idx, Tk, E, block_hist);
   int rc = check_launch();
   if (rc) return rc;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, block_hist, nb, E, Tk,
-                     counts, offsets);
+  hipLaunchKernelGGL(dispatch_rows_kernel, dim3((E + 3) / 4), dim3(kDispThreads), 0, st,
+                     block_hist, nb, E, counts);
   rc = check_launch();
   if (rc) return rc;
-  const size_t lds = 4 * (size_t)E * sizeof(int);
+  const size_t lds = 5 * (size_t)E * sizeof(int);
   if (E <= 256)
     hipLaunchKernelGGL(dispatch_scatter_kernel<8>, dim3(nb), dim3(kDispThreads), lds, st, idx, Tk,
-                       E, block_hist, perm, inv_perm);
+                       E, block_hist, counts, offsets, perm, inv_perm);
   else
     hipLaunchKernelGGL(dispatch_scatter_kernel<10>, dim3(nb), dim3(kDispThreads), lds, st, idx,
-                       Tk, E, block_hist, perm, inv_perm);
+                       Tk, E, block_hist, counts, offsets, perm, inv_perm);
   return check_launch();
 }
 

@@ -19,31 +19,72 @@
 
 namespace moe {
 
-template <int PL>
+template <int PL, int U>
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restrict__ col_bias,
             float* __restrict__ logits_out, const float* __restrict__ bias, int T, int E,
             int k, float scaling, int32_t* __restrict__ idx, float* __restrict__ gate) {
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
 
   // logits = sum of the K-split partials in split order (+ classifier offset)
   float l[PL];
   float m = -INFINITY;
+  if constexpr (U == 1) {
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) {
-      float v = partials[(size_t)t * E + e];
-      for (int sp = 1; sp < nsplit; ++sp) v += partials[((size_t)sp * T + t) * E + e];
-      if (col_bias != nullptr) v += col_bias[e];
-      if (logits_out != nullptr) logits_out[(size_t)t * E + e] = v;
-      l[i] = v;
-    } else {
-      l[i] = -INFINITY;
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        float v = partials[(size_t)t * E + e];
+        for (int sp = 1; sp < nsplit; ++sp) v += partials[((size_t)sp * T + t) * E + e];
+        if (col_bias != nullptr) v += col_bias[e];
+        if (logits_out != nullptr) logits_out[(size_t)t * E + e] = v;
+        l[i] = v;
+      } else {
+        l[i] = -INFINITY;
+      }
+      m = fmaxf(m, l[i]);
     }
-    m = fmaxf(m, l[i]);
+  } else {
+    // many splits and few tokens: read U splits at a time so the loads overlap
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      l[i] = e < E ? partials[(size_t)t * E + e] : 0.f;
+    }
+    int sp = 1;
+    for (; sp + U <= nsplit; sp += U) {
+      float v[U][PL];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+          const int e = lane + 64 * i;
+          v[u][i] = e < E ? partials[((size_t)(sp + u) * T + t) * E + e] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < PL; ++i) l[i] += v[u][i];
+    }
+    for (; sp < nsplit; ++sp)
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) l[i] += partials[((size_t)sp * T + t) * E + e];
+      }
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        if (col_bias != nullptr) l[i] += col_bias[e];
+        if (logits_out != nullptr) logits_out[(size_t)t * E + e] = l[i];
+      } else {
+        l[i] = -INFINITY;
+      }
+      m = fmaxf(m, l[i]);
+    }
   }
   m = wave_max(m);
   float s = 0.f;
@@ -113,18 +154,28 @@ topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restr
 int launch_topk(const float* partials, int nsplit, const float* col_bias, float* logits_out,
                 const float* bias, int T, int E, int k, float scaling, int32_t* idx, float* gate,
                 hipStream_t st) {
-  const dim3 grid((T + 3) / 4), block(256);
+  // few tokens (decode): one wave per workgroup, spread over more CUs
+  const int wpb = T < 2048 ? 1 : 4;
+  const dim3 grid((T + wpb - 1) / wpb), block(64 * wpb);
 #define MOE_TOPK_ARGS partials, nsplit, col_bias, logits_out, bias, T, E, k, scaling, idx, gate
+#define MOE_TOPK(PL)                                                                   \
+  do {                                                                                \
+    if (nsplit >= 4)                                                                  \
+      hipLaunchKernelGGL((topk_kernel<PL, 4>), grid, block, 0, st, MOE_TOPK_ARGS);    \
+    else                                                                              \
+      hipLaunchKernelGGL((topk_kernel<PL, 1>), grid, block, 0, st, MOE_TOPK_ARGS);    \
+  } while (0)
   if (E <= 64)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, st, MOE_TOPK_ARGS);
+    MOE_TOPK(1);
   else if (E <= 128)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, MOE_TOPK_ARGS);
+    MOE_TOPK(2);
   else if (E <= 256)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, st, MOE_TOPK_ARGS);
+    MOE_TOPK(4);
   else if (E <= 512)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, MOE_TOPK_ARGS);
+    MOE_TOPK(8);
   else
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, st, MOE_TOPK_ARGS);
+    MOE_TOPK(16);
+#undef MOE_TOPK
 #undef MOE_TOPK_ARGS
   return check_launch();
 }
