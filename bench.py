@@ -12,6 +12,14 @@ The default workload is T=4096 tokens, d_model=2048, 64 SwiGLU experts
 PID set point 6 real experts/token (Kp=0.01, Ki=0.001, Kd=0) updated after
 every batch; the timed steps are batches 0..K-1 of that run, starting from
 the initial bias (warm-up steps run first and are then undone).
+
+The timed steps record three HIP events each (step start, gate/up start and
+end: each record costs GPU time).  After them, outside the timed region, the
+same steps are replayed once with an event at every stage boundary
+(stages_ms_mean) and every step's expert loads logged (exact assignments and
+touched experts per step for the roofline, load variance per batch), and,
+for the workloads whose data can stay in L2 / Infinity Cache, once more
+with 512 MiB written between steps ("cold", event-timed steps only).
 """
 
 from __future__ import annotations
@@ -55,6 +63,19 @@ def gate_up_units(w, A, U):
     flops = 4.0 * A * w.d_model * w.d_ff
     byts = el * (2.0 * U * w.d_ff * w.d_model + A * w.d_model + A * w.d_ff)
     return flops, byts
+
+
+def gate_up_kernel_name(w):
+    """Which gate/up kernel the library launches for this shape (the same
+    test the library makes: bf16, at least 32 assignments per expert, both K
+    lengths multiples of 128)."""
+    E = w.n_ffn + w.n_zero
+    if (w.dtype == "bf16" and (w.T * w.top_k) // E >= 32 and w.d_model % 128 == 0
+            and w.d_ff % 128 == 0):
+        return "grouped_gemm_big_kernel<1,4> (256x256 tiles, gate/up + SwiGLU)"
+    if (w.T * w.top_k) // E >= 32:
+        return "grouped_gemm_kernel mode 1 (128x128 tiles, gate/up + SwiGLU)"
+    return "grouped_gemm_kernel mode 1 (16x128 tiles, gate/up + SwiGLU)"
 
 
 def measured_traffic(workload):
@@ -141,24 +162,28 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
+        """One step; ev: None, 7 events (every stage boundary) or 3 events
+        (step start, gate/up start, gate/up end: the timed run keeps its
+        event count low, since each record costs GPU time)."""
         x = xs[i % len(xs)]
+        full = ev is not None and len(ev) == 7
         if ev is not None:
             ev[0].record(stream)
         B.moe_route(shape, x, wr, lb, bias, buf.topk_idx, buf.topk_gate, None, buf.ws)
-        if ev is not None:
+        if full:
             ev[1].record(stream)
         B.moe_dispatch(shape, buf.topk_idx, x, buf.counts, buf.offsets, buf.perm,
                        buf.inv_perm, None, buf.ws)
         if ev is not None:
-            ev[2].record(stream)
+            ev[2 if full else 1].record(stream)
         B.moe_ffn_gate_up(shape, x, None, buf.perm, buf.offsets, wg, wu, buf.ws)
         if ev is not None:
-            ev[3].record(stream)
+            ev[3 if full else 2].record(stream)
         B.moe_ffn_down(shape, buf.offsets, wd, buf.y_perm, buf.ws)
-        if ev is not None:
+        if full:
             ev[4].record(stream)
         B.moe_combine(shape, x, buf.y_perm, buf.topk_idx, buf.topk_gate, buf.inv_perm, buf.y)
-        if ev is not None:
+        if full:
             ev[5].record(stream)
         if params is not None:
             B.moe_pid_update(shape, params, buf.counts, buf.pid_state, bias, r_log,
@@ -166,8 +191,8 @@ def main():
         if args.balance > 0:
             B.moe_balance_update(shape, args.balance, buf.counts, bias)
         if load_log is not None:
-            load_log[i % load_log.shape[0]].copy_(buf.counts[: w.n_ffn])
-        if ev is not None:
+            load_log[i % load_log.shape[0]].copy_(buf.counts)
+        if full:
             ev[6].record(stream)
 
     load_log = None
@@ -182,31 +207,68 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    if args.balance > 0:
-        # per-step FFN loads for the load-gap report (a small device copy per step)
-        load_log = torch.zeros((K, w.n_ffn), dtype=torch.int32, device=dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(i, evs[i])
+    ev_end.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    # ---- per-stage durations (HIP events on the launch stream)
+    # ---- timed-run durations (HIP events on the launch stream): each step
+    # (start to next start) and each gate/up launch
+    starts = [evs[i][0] for i in range(K)] + [ev_end]
+    step_ms = np.array([starts[i].elapsed_time(starts[i + 1]) for i in range(K)])
+    gu_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
+
+    def reset_controller():
+        bias.copy_(bias0)
+        buf.pid_state.zero_()
+        r_log.zero_()
+        torch.cuda.synchronize()
+
+    # ---- untimed replay of the same K steps (same inputs, same controller
+    # trajectory) with an event at every stage boundary and each step's
+    # expert loads logged: the stage breakdown and exact per-step A and U
+    reset_controller()
+    load_log = torch.zeros((K, w.n_ffn + w.n_zero), dtype=torch.int32, device=dev)
+    revs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    for i in range(K):
+        step(i, revs[i])
+    torch.cuda.synchronize()
     names = ["route", "dispatch", "ffn_gate_up", "ffn_down", "combine", "pid"]
-    st_ms = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]
+    st_ms = {n: [revs[i][j].elapsed_time(revs[i][j + 1]) for i in range(K)]
              for j, n in enumerate(names)}
-    counts = buf.counts.cpu().numpy()
-    if w.pid:
-        A = np.rint(r_log.cpu().numpy()[:K] * w.T).astype(np.int64)
-        U = np.full(K, int((counts[: w.n_ffn] > 0).sum()))  # last batch's touched experts
-    else:
-        A = np.full(K, int(counts[: w.n_ffn].sum()))
-        U = np.full(K, int((counts[: w.n_ffn] > 0).sum()))
+    loads = load_log.cpu().numpy().astype(np.int64)
+    load_log = None
+    A = loads[:, : w.n_ffn].sum(axis=1)
+    U = (loads[:, : w.n_ffn] > 0).sum(axis=1)
+
+    # ---- cold pass: 512 MiB written between steps evicts L2 and the
+    # Infinity Cache, so every step starts from HBM (events time the step
+    # only); for the workloads whose data can stay cache-resident
+    cold = None
+    if w.name in ("tiny_f32", "small_bf16", "skewed_bf16"):
+        reset_controller()
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+        for i in range(K):
+            scratch.fill_(i & 255)
+            step(i, cevs[i])
+        torch.cuda.synchronize()
+        del scratch
+        c_ms = np.array([cevs[i][0].elapsed_time(cevs[i][6]) for i in range(K)])
+        cold = {"ms_per_step_median": float(np.median(c_ms)),
+                "tokens_per_s_median": w.T / (float(np.median(c_ms)) * 1e-3),
+                "ffn_gate_up_ms_mean": float(np.mean(
+                    [cevs[i][2].elapsed_time(cevs[i][3]) for i in range(K)]))}
+    reset_controller()
+
     fl, by = zip(*[gate_up_units(w, int(a), int(u)) for a, u in zip(A, U)])
-    gu_s = np.array(st_ms["ffn_gate_up"]) / 1e3
+    gu_s = gu_ms / 1e3
     peak_fl = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32_MFMA
     t_fl = np.sum(fl) / peak_fl
     t_by = np.sum(by) / PEAK_HBM
@@ -218,8 +280,7 @@ def main():
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "grouped_gemm_kernel (gate/up + SwiGLU), mean %.4f ms/launch" % (
-        gu_s.mean() * 1e3)
+    roof["kernel"] = "%s, mean %.4f ms/launch" % (gate_up_kernel_name(w), gu_s.mean() * 1e3)
 
     tokens = w.T * K
     value = tokens / elapsed
@@ -240,17 +301,23 @@ def main():
                    "n_zero": w.n_zero, "d_ff": w.d_ff, "top_k": w.top_k,
                    "pid": list(w.pid) if w.pid else None},
         "roofline": roof,
+        "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
+                    "p90": float(np.percentile(step_ms, 90))},
         "stages_ms_mean": {n: float(np.mean(v)) for n, v in st_ms.items()},
         "ffn_assignments_per_step_mean": float(np.mean(A)),
+        "touched_ffn_experts_per_step_mean": float(np.mean(U)),
     }
+    if cold is not None:
+        line["cold"] = cold
     if w.pid:
-        line["r_per_step"] = [round(float(v), 4) for v in r_log.cpu().numpy()[:K]]
-    if load_log is not None:
-        ll = load_log.cpu().numpy().astype(np.float64)
-        line["balance_gamma"] = args.balance
+        line["r_per_step"] = [round(float(a) / w.T, 4) for a in A]
+        line["ms_per_batch"] = [round(float(v), 4) for v in step_ms]
+        ll = loads[:, : w.n_ffn].astype(np.float64)
         line["ffn_load_max_over_mean_per_step"] = [
             round(float(r.max() / max(r.mean(), 1e-9)), 2) for r in ll]
         line["ffn_load_variance_per_step"] = [round(float(r.var()), 1) for r in ll]
+    if args.balance > 0:
+        line["balance_gamma"] = args.balance
 
     if not args.no_cpu_baseline and w.name in ("small_bf16", "skewed_bf16", "tiny_f32"):
         m = dict(wr=wr, lb=lb, bias0=bias0, wg=wg, wu=wu, wd=wd, xs=xs)
