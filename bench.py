@@ -49,6 +49,10 @@ def parse():
                     choices=["small_bf16", "decode_bf16", "prefill_bf16", "skewed_bf16",
                              "tiny_f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--scmoe", type=int, default=0, metavar="D_FF",
+                    help="shortcut-connected block: time the MoE layer against a dense "
+                         "SwiGLU branch of this width on a second stream (e.g. 12288); "
+                         "0 = off")
     ap.add_argument("--balance", type=float, default=0.0,
                     help="per-expert load-balancing step (moe_balance_update) after the PID; "
                          "0 = off")
@@ -67,13 +71,17 @@ def gate_up_units(w, A, U):
 
 def gate_up_kernel_name(w):
     """Which gate/up kernel the library launches for this shape (the same
-    test the library makes: bf16, at least 32 assignments per expert, both K
-    lengths multiples of 128)."""
+    tests the library makes: at least 32 assignments per expert and at least
+    64 tiles for the tall tiles; bf16 and both K lengths multiples of 128 for
+    the 256x256 direct-to-LDS tiles)."""
     E = w.n_ffn + w.n_zero
-    if (w.dtype == "bf16" and (w.T * w.top_k) // E >= 32 and w.d_model % 128 == 0
-            and w.d_ff % 128 == 0):
+    Tk = w.T * w.top_k
+    cdiv = lambda a, b: -(-a // b)  # noqa: E731
+    tall = Tk // E >= 32 and cdiv(Tk, 128) * cdiv(min(w.d_ff, w.d_model), 128) >= 64
+    if (tall and w.dtype == "bf16" and w.d_model % 128 == 0 and w.d_ff % 128 == 0
+            and cdiv(Tk, 256) * min(w.d_ff // 128, w.d_model // 256) >= 64):
         return "grouped_gemm_big_kernel<1,4> (256x256 tiles, gate/up + SwiGLU)"
-    if (w.T * w.top_k) // E >= 32:
+    if tall:
         return "grouped_gemm_kernel mode 1 (128x128 tiles, gate/up + SwiGLU)"
     return "grouped_gemm_kernel mode 1 (16x128 tiles, gate/up + SwiGLU)"
 
@@ -124,12 +132,108 @@ def cpu_baseline(w, m, budget_s=12.0):
     return n_tok / t_total, threads, t_total, nb
 
 
+def scmoe_main(args):
+    """MoE layer and the dense SwiGLU branch of a shortcut-connected block:
+    each alone, one after the other on one stream, and concurrently on two
+    streams (default priorities).  One step = the layer and the branch over
+    one batch; value = tokens/s of the concurrent steps."""
+    import numpy as np
+    import torch
+
+    from sparse_moe_layer_03_amd import binding as B
+    from sparse_moe_layer_03_amd import scmoe
+    from sparse_moe_layer_03_amd import synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    w = S.WORKLOADS[args.workload]
+    if w.pid or w.zipf_s:
+        print("--scmoe runs the decode/prefill workloads (fixed router bias)", file=sys.stderr)
+        sys.exit(2)
+    wr = S.make_router(w, dev)
+    bias = S.make_bias(w, dev)
+    wg, wu, wd = S.make_experts(w, dev)
+    x = S.make_x(w, 0, dev)
+    w1, w3, w2 = S.make_dense(w, args.scmoe, dev)
+    shape = B.make_shape(w.T, w.d_model, w.n_ffn, w.n_zero, w.d_ff, w.top_k, w.dtype,
+                         w.routed_scaling)
+    buf = B.LayerBuffers(shape, dev)
+    br = scmoe.DenseBranch(w.T, w.d_model, args.scmoe, w.dtype, dev)
+    main_s = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+
+    def moe():
+        B.layer_forward(buf, x, wr, bias, wg, wu, wd)
+
+    def dense(stream=None):
+        br.run(x, w1, w3, w2, stream=stream)
+
+    def both_serial():
+        moe()
+        dense()
+
+    def both_concurrent():
+        side.wait_stream(main_s)
+        moe()
+        with torch.cuda.stream(side):
+            dense(side)
+        main_s.wait_stream(side)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    # interleave the modes over three rounds; keep each mode's best round
+    res = {k: [] for k in ("moe", "dense", "serial", "concurrent")}
+    for _ in range(3):
+        res["moe"].append(timed(moe))
+        res["dense"].append(timed(dense))
+        res["serial"].append(timed(both_serial))
+        res["concurrent"].append(timed(both_concurrent))
+    ms = {k: float(np.min(v)) for k, v in res.items()}
+    dense_flops = 6.0 * w.T * w.d_model * args.scmoe
+    line = {
+        "metric": METRIC + " (shortcut-connected block: MoE layer || dense FFN branch)",
+        "value": w.T / (ms["concurrent"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms["concurrent"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/d_in) weights)",
+        "config": {"workload": f"{w.name}+dense{args.scmoe}", "T": w.T, "d_model": w.d_model,
+                   "n_ffn": w.n_ffn, "n_zero": w.n_zero, "d_ff": w.d_ff, "top_k": w.top_k,
+                   "dense_d_ff": args.scmoe},
+        "scmoe": {"moe_ms": ms["moe"], "dense_ms": ms["dense"], "serial_ms": ms["serial"],
+                  "concurrent_ms": ms["concurrent"],
+                  "saved_ms": ms["serial"] - ms["concurrent"],
+                  "dense_hidden_frac": (ms["serial"] - ms["concurrent"]) / ms["dense"],
+                  "dense_weight_gb_per_s": 3.0 * w.d_model * args.scmoe
+                  * (2 if w.dtype == "bf16" else 4) / (ms["dense"] * 1e-3) / 1e9,
+                  "dense_tflop_per_s": dense_flops / (ms["dense"] * 1e-3) / 1e12,
+                  "rounds_ms": res},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+    if args.scmoe:
+        return scmoe_main(args)
 
     import numpy as np
     import torch

@@ -83,22 +83,32 @@ static WsLayout ws_layout(const moe_shape* s) {
   return w;
 }
 
-// Few rows per expert -> 16-row tiles; otherwise 128x128 tiles.
+// Tile shape of the expert GEMMs.  Rows per expert (T*k/E) of at least 32
+// make tall tiles worth it, but only if there are enough of them to spread
+// over the chip: a dense batch of 128 rows through one expert (T*k/E = 128)
+// gives a single row of tiles, so 16-row tiles are used for it.
+static long cdiv(long a, long b) { return (a + b - 1) / b; }
+static constexpr long kMinTiles = 64;
+
+// 128x128 tiles (else 16x128) for the general kernel.
 static int ffn_big_tiles(const moe_shape* s) {
   const long E = (long)s->n_ffn + s->n_zero;
-  return ((long)s->T * s->top_k) / E >= 32;
+  const long Tk = (long)s->T * s->top_k;
+  return Tk / E >= 32 && cdiv(Tk, 128) * cdiv(std::min(s->d_ff, s->d_model), 128) >= kMinTiles;
 }
 
-// The many-row expert GEMMs (gate/up and down together: down reads the tile
-// list gate/up writes) need bf16, both K lengths a multiple of 128 (K-steps
-// of 64 in pairs), and every operand byte offset within 32 bits (token rows
-// may come from x_perm, which has T*k rows).
+// The many-row expert GEMMs (gate/up and down together) need bf16, both K
+// lengths a multiple of 128 (K-steps of 64 in pairs), every operand byte
+// offset within 32 bits (token rows may come from x_perm, which has T*k
+// rows), and enough 256x256 tiles.
 static bool ffn_use_big(const moe_shape* s) {
   const size_t Tk = (size_t)s->T * s->top_k;
   if (!(ffn_big_tiles(s) && s->dtype == MOE_BF16 && s->d_model % 128 == 0 &&
         s->d_ff % 128 == 0 && Tk * s->d_model * 2 < (1ull << 32) &&
         Tk * s->d_ff * 2 < (1ull << 32) && (size_t)s->d_ff * s->d_model * 2 < (1ull << 32)))
     return false;
+  const long nt_min = std::min((long)s->d_ff / 128, (long)s->d_model / 256);
+  if (cdiv((long)Tk, 256) * nt_min < kMinTiles) return false;
   // each workgroup tracks at most 128 tiles (gate/up: d_ff/128 column
   // tiles per m-tile, down: d_model/256); the m-tile count of the first
   // group is packed into 22 bits

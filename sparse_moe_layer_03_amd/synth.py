@@ -16,6 +16,8 @@ Recipe (value distributions follow each workload's statement):
   W_up      ~ N(0, 1/d_model)            tag 5, index = expert
   W_down    ~ N(0, 1/d_ff)               tag 6, index = expert
   Zipf rank permutation of FFN experts   tag 7
+  dense branch W1, W3 ~ N(0, 1/d_model)  tags 8, 9 (shortcut-connected block)
+  dense branch W2     ~ N(0, 1/d_ff)     tag 10
 N(m, v) names mean and variance.
 """
 
@@ -28,6 +30,7 @@ from typing import Optional
 import torch
 
 TAG_X, TAG_WR, TAG_BIAS, TAG_WG, TAG_WU, TAG_WD, TAG_ZIPF = 1, 2, 3, 4, 5, 6, 7
+TAG_D1, TAG_D3, TAG_D2 = 8, 9, 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -132,6 +135,17 @@ def make_experts(w: Workload, device="cpu", experts=None):
         wu[i] = normal((w.d_ff, w.d_model), s_in, dt, device, w.seed, TAG_WU, e)
         wd[i] = normal((w.d_model, w.d_ff), s_ff, dt, device, w.seed, TAG_WD, e)
     return wg, wu, wd
+
+
+def make_dense(w: Workload, d_ff: int, device="cpu"):
+    """Dense SwiGLU branch weights W1, W3 [d_ff, d] and W2 [d, d_ff] of a
+    shortcut-connected block (the dense FFN beside the MoE layer)."""
+    dt = torch_dtype(w.dtype)
+    s_in, s_ff = 1.0 / math.sqrt(w.d_model), 1.0 / math.sqrt(d_ff)
+    w1 = normal((d_ff, w.d_model), s_in, dt, device, w.seed, TAG_D1, 0)
+    w3 = normal((d_ff, w.d_model), s_in, dt, device, w.seed, TAG_D3, 0)
+    w2 = normal((w.d_model, d_ff), s_ff, dt, device, w.seed, TAG_D2, 0)
+    return w1, w3, w2
 
 
 def zipf_logit_offset(w: Workload, alpha: float, device="cpu"):

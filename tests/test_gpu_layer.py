@@ -58,10 +58,11 @@ def test_small_bf16_workload_batch0():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [
     # T, d, N, Z, d_ff, k   -- several tiles with ragged tails in M and N
-    (600, 192, 32, 8, 320, 4),     # 128x128 tiles (>= 32 rows per expert)
+    (1600, 192, 32, 8, 320, 4),    # 128x128 tiles (>= 32 rows per expert, >= 64 tiles)
     (77, 256, 40, 24, 192, 6),     # 16-row tiles
     (1, 64, 3, 1, 64, 2),          # single token
-    (1000, 384, 16, 8, 384, 4),    # bf16: 256x256 direct-to-LDS tiles, 2 m-tiles/expert
+    (2048, 512, 16, 8, 384, 4),    # bf16: 256x256 direct-to-LDS tiles, 2 m-tiles/expert,
+                                   # K-steps 8 (gate/up) and 6 (down)
 ])
 def test_ragged_shapes(dtype, shape):
     T, d, N, Z, dff, k = shape

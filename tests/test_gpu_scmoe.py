@@ -1,0 +1,87 @@
+"""Dense SwiGLU branch of a shortcut-connected block, through the library's
+one-expert FFN call, and its overlap with the MoE layer on two streams.
+
+Oracle: the textbook dense SwiGLU FFN (oracle swiglu_ffn over all tokens).
+Overlap: running the MoE layer and the dense branch concurrently on two
+streams must give bitwise the outputs of running them one after the other
+(the kernels are deterministic and share no buffers)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_moe_layer_03_amd import binding as B
+from sparse_moe_layer_03_amd import scmoe
+from sparse_moe_layer_03_amd import synth as S
+from tests.parity_util import Model, row_rel_l2, run_gpu, say, tolerances
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T,d,dff,dtype", [
+    (64, 128, 256, "f32"),
+    (300, 512, 768, "bf16"),     # 16-row tiles, ragged last tile
+    (8192, 512, 1024, "bf16"),   # 256x256 direct-to-LDS tiles (many rows, one expert)
+])
+def test_dense_branch_matches_oracle(T, d, dff, dtype):
+    w = S.Workload("dense", T=T, d_model=d, n_ffn=1, n_zero=0, d_ff=dff, top_k=1, dtype=dtype,
+                   seed=5)
+    say(f"dense branch T={T} d={d} d_ff={dff} {dtype}")
+    x = S.make_x(w, 0, "cuda")
+    w1, w3, w2 = S.make_dense(w, dff, "cuda")
+    br = scmoe.DenseBranch(T, d, dff, dtype)
+    y = br.run(x, w1, w3, w2)
+    torch.cuda.synchronize()
+    ref = O.swiglu_ffn(S.to_numpy64(x), S.to_numpy64(w1), S.to_numpy64(w3), S.to_numpy64(w2))
+    err = row_rel_l2(S.to_numpy64(y), ref)
+    say(f"  max row rel L2 {err.max():.3e}")
+    assert err.max() <= tolerances(dtype)["y"]
+
+
+def test_dense_branch_decode_shape_sampled_rows():
+    # T = 128 tokens of width 6144 through a 12,288-wide dense FFN
+    w = S.Workload("dense_decode", T=128, d_model=6144, n_ffn=1, n_zero=0, d_ff=12288, top_k=1,
+                   dtype="bf16", seed=5)
+    say("dense branch decode shape")
+    x = S.make_x(w, 0, "cuda")
+    w1, w3, w2 = S.make_dense(w, w.d_ff, "cuda")
+    br = scmoe.DenseBranch(w.T, w.d_model, w.d_ff, "bf16")
+    y = br.run(x, w1, w3, w2)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(0).choice(w.T, 16, replace=False)
+    ref = O.swiglu_ffn(S.to_numpy64(x[rows]), S.to_numpy64(w1), S.to_numpy64(w3),
+                       S.to_numpy64(w2))
+    err = row_rel_l2(S.to_numpy64(y[rows]), ref)
+    say(f"  max row rel L2 {err.max():.3e}")
+    assert err.max() <= tolerances("bf16")["y"]
+
+
+def test_moe_and_dense_on_two_streams_match_serial():
+    w = S.Workload("scmoe", T=512, d_model=512, n_ffn=16, n_zero=8, d_ff=256, top_k=4,
+                   dtype="bf16", bias_var=0.01, seed=7)
+    say("MoE layer || dense branch on two streams")
+    m = Model(w)
+    x = S.make_x(w, 0, "cuda")
+    w1, w3, w2 = S.make_dense(w, 1536, "cuda")
+    br = scmoe.DenseBranch(w.T, w.d_model, 1536, "bf16")
+
+    buf = B.LayerBuffers(m.shape, "cuda")
+    run_gpu(m, x, buf, with_logits=False)
+    y_dense = br.run(x, w1, w3, w2).clone()
+    torch.cuda.synchronize()
+    y_moe = buf.y.clone()
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()  # default priority
+    for rep in range(3):
+        buf.y.zero_()
+        br.y.zero_()
+        side.wait_stream(main)
+        B.layer_forward(buf, x, m.wr, m.bias, m.wg, m.wu, m.wd)  # main stream, no sync
+        with torch.cuda.stream(side):
+            br.run(x, w1, w3, w2, stream=side)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(buf.y, y_moe), rep
+        assert torch.equal(br.y, y_dense), rep
