@@ -160,6 +160,9 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
     return MOE_EALIGN;
   hipStream_t st = (hipStream_t)stream;
   const int E = s->n_ffn + s->n_zero;
+  if (router_topk_fused_ok(s->T, E, s->d_model, s->dtype))
+    return launch_router_topk(x, w_router, logit_bias, logits_out, bias, s->T, E, s->d_model,
+                              s->top_k, s->routed_scaling, topk_idx, topk_gate, st);
   const int nsplit = router_ksplit(s->T, E, s->d_model, s->dtype);
   float* partials = (float*)((char*)ws + ws_layout(s).logits);
   GemmArgs g{};

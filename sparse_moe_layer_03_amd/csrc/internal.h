@@ -46,6 +46,13 @@ int launch_topk(const float* partials, int nsplit, const float* col_bias, float*
                 const float* bias, int T, int E, int k, float scaling, int32_t* idx, float* gate,
                 hipStream_t st);
 
+// Router GEMM + top-k in one launch (bf16, at most 128 experts, d_model a
+// multiple of 512).
+bool router_topk_fused_ok(int T, int E, int d_model, int dtype);
+int launch_router_topk(const void* x, const void* wr, const float* col_bias, float* logits_out,
+                       const float* bias, int T, int E, int d, int k, float scaling,
+                       int32_t* idx, float* gate, hipStream_t st);
+
 // K split of the router GEMM for a shape (depends on the shape only).
 int router_ksplit(int T, int E, int d_model, int dtype);
 

@@ -19,6 +19,107 @@
 
 namespace moe {
 
+// Softmax, biased top-k and gates of NT tokens held by one wave (lane holds
+// experts lane + 64 i of each; m[n] is the lane's partial max of token n);
+// writes token t[n]'s k slots of idx / gate in ascending expert id, for the
+// tokens with t[n] >= 0.  The NT tokens' reductions are independent chains
+// interleaved step by step, so their shuffle latencies overlap.
+template <int PL, int NT>
+__device__ __forceinline__ void select_topk(float (&l)[NT][PL], float (&m)[NT],
+                                            const float* __restrict__ bias, int E, int k,
+                                            float scaling, const int (&t)[NT],
+                                            int32_t* __restrict__ idx, float* __restrict__ gate) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) m[n] = fmaxf(m[n], __shfl_xor(m[n], o, kWave));
+  float s[NT], p[NT][PL];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    s[n] = 0.f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      p[n][i] = (e < E) ? expf(l[n][i] - m[n]) : 0.f;
+      s[n] += p[n][i];
+    }
+  }
+  // same butterfly order as wave_sum
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) s[n] += __shfl_xor(s[n], o, kWave);
+  float key[NT][PL];
+  bool avail[NT][PL], sel[NT][PL];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      p[n][i] = p[n][i] / s[n];
+      avail[n][i] = e < E;
+      sel[n][i] = false;
+      key[n][i] = avail[n][i] ? p[n][i] + bias[e] : 0.f;
+      if (key[n][i] != key[n][i]) key[n][i] = -INFINITY;  // NaN never outranks a number
+    }
+
+  for (int r = 0; r < k; ++r) {
+    float bk[NT];
+    int bid[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      bk[n] = -INFINITY;
+      bid[n] = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int e = lane + 64 * i;
+        if (avail[n][i] && (key[n][i] > bk[n] || (key[n][i] == bk[n] && e < bid[n]))) {
+          bk[n] = key[n][i];
+          bid[n] = e;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float ok = __shfl_xor(bk[n], o, kWave);
+        const int oid = __shfl_xor(bid[n], o, kWave);
+        if (ok > bk[n] || (ok == bk[n] && oid < bid[n])) {
+          bk[n] = ok;
+          bid[n] = oid;
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      if ((bid[n] & 63) == lane) {
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+          if (i == (bid[n] >> 6)) {
+            avail[n][i] = false;
+            sel[n][i] = true;
+          }
+      }
+  }
+
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    int pos = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const uint64_t bal = __ballot(sel[n][i]);
+      if (sel[n][i] && t[n] >= 0) {
+        const int o = t[n] * k + pos + __popcll(bal & lanemask_lt());
+        idx[o] = lane + 64 * i;
+        gate[o] = scaling * p[n][i];
+      }
+      pos += __popcll(bal);
+    }
+  }
+}
+
 template <int PL, int U>
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restrict__ col_bias,
@@ -86,69 +187,144 @@ topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restr
       m = fmaxf(m, l[i]);
     }
   }
-  m = wave_max(m);
-  float s = 0.f;
-  float p[PL];
+  float l1[1][PL], m1[1] = {m};
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = lane + 64 * i;
-    p[i] = (e < E) ? expf(l[i] - m) : 0.f;
-    s += p[i];
-  }
-  s = wave_sum(s);
-  float key[PL];
-  bool avail[PL], sel[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = lane + 64 * i;
-    p[i] = p[i] / s;
-    avail[i] = e < E;
-    sel[i] = false;
-    key[i] = avail[i] ? p[i] + bias[e] : 0.f;
-    if (key[i] != key[i]) key[i] = -INFINITY;  // NaN never outranks a number
-  }
+  for (int i = 0; i < PL; ++i) l1[0][i] = l[i];
+  const int t1[1] = {t};
+  select_topk<PL, 1>(l1, m1, bias, E, k, scaling, t1, idx, gate);
+}
 
-  for (int r = 0; r < k; ++r) {
-    float bk = -INFINITY;
-    int bid = 0x7fffffff;
+// Router GEMM and top-k in one launch, for at most 128 experts in bf16
+// (d_model a multiple of 128 * NW).  A workgroup takes 16 tokens and all
+// experts (in ceil(E / 16) column blocks of 16).  Wave w of NW multiplies them by the router over the K slice w
+// with v_mfma_f32_16x16x32_bf16, operands loaded straight from global memory
+// into registers with P K-steps of 32 in flight; the slices' products are
+// summed in LDS in slice order, and each wave then selects for 16/NW of the
+// tokens at once.  Every workgroup reads the whole router matrix, so the
+// limit is how many loads each CU keeps in flight: hence NW waves.
+template <int NCB, int NW>
+__global__ void __launch_bounds__(64 * NW)
+router_topk_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ wr,
+                   const float* __restrict__ col_bias, float* __restrict__ logits_out,
+                   const float* __restrict__ bias, int T, int E, int d, int k, float scaling,
+                   int32_t* __restrict__ idx, float* __restrict__ gate) {
+  // NCB 16-expert column blocks (E <= 16 NCB); PL experts per lane in the
+  // selection
+  constexpr int PL = (NCB * 16 + 63) / 64;
+  constexpr int BT = 16;            // tokens per workgroup
+  constexpr int TPW = BT / NW;      // tokens selected per wave
+  constexpr int P = 4;              // K-steps in flight
+  constexpr int LDP = NCB * 16 + 4; // LDS row pitch (floats): conflict-free stores
+  static_assert(BT % NW == 0, "tokens per wave");
+  __shared__ float s_part[NW][BT][LDP];
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t0 = blockIdx.x * BT;
+  const int r16 = lane & 15, oct = lane >> 4;  // operand row / col, K octet
+  const int kq = d / NW;                       // K per wave
+  const int nsteps = kq / 32;                  // multiple of P (host: d % (128 NW) == 0)
+
+  // lane's operand rows: token t0 + r16 (A), expert 16c + r16 (B); rows past
+  // the end are clamped (their products are never used)
+  const int xr = min(t0 + r16, T - 1);
+  const char* xa = (const char*)x + ((size_t)xr * d + (size_t)w * kq + oct * 8) * 2;
+  uint32_t wo[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    const int e = min(16 * c + r16, E - 1);
+    wo[c] = (uint32_t)(((size_t)e * d + (size_t)w * kq + oct * 8) * 2);
+  }
+  const char* wb = (const char*)wr;
+
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4_t fx[P], fw[P][NCB];
+  auto fetch = [&](int slot, int st) __attribute__((always_inline)) {
+    fx[slot] = *reinterpret_cast<const u32x4_t*>(xa + st * 64);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+      fw[slot][c] = *reinterpret_cast<const u32x4_t*>(wb + wo[c] + st * 64);
+  };
+#pragma unroll
+  for (int u = 0; u < P; ++u) fetch(u, u);
+  for (int st = 0; st < nsteps; st += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, fx[u]), __builtin_bit_cast(bf16x8_t, fw[u][c]),
+            acc[c], 0, 0, 0);
+      // unconditional (clamped past the end, never used): a conditional load
+      // makes the compiler drain every load in flight at the loop head
+      fetch(u, min(st + u + P, nsteps - 1));
+    }
+  }
+  // lane holds C[4 oct + i][r16] of each column block: tokens 4 oct + i
+#pragma unroll
+  for (int c = 0; c < NCB; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[w][4 * oct + i][16 * c + r16] = acc[c][i];
+  __syncthreads();
+
+  // wave w selects for tokens TPW w .. TPW w + TPW - 1 together
+  float l[TPW][PL], m[TPW];
+  int tk[TPW];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int tt = TPW * w + q, t = t0 + tt;
+    tk[q] = t < T ? t : -1;
+    m[q] = -INFINITY;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int e = lane + 64 * i;
-      if (avail[i] && (key[i] > bk || (key[i] == bk && e < bid))) {
-        bk = key[i];
-        bid = e;
-      }
-    }
+      if (e < E) {
+        float v = s_part[0][tt][e];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ok = __shfl_xor(bk, o, kWave);
-      const int oid = __shfl_xor(bid, o, kWave);
-      if (ok > bk || (ok == bk && oid < bid)) {
-        bk = ok;
-        bid = oid;
+        for (int ww = 1; ww < NW; ++ww) v += s_part[ww][tt][e];
+        if (col_bias != nullptr) v += col_bias[e];
+        if (logits_out != nullptr && t < T) logits_out[(size_t)t * E + e] = v;
+        l[q][i] = v;
+      } else {
+        l[q][i] = -INFINITY;
       }
-    }
-    if ((bid & 63) == lane) {
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (i == (bid >> 6)) {
-          avail[i] = false;
-          sel[i] = true;
-        }
+      m[q] = fmaxf(m[q], l[q][i]);
     }
   }
+  select_topk<PL, TPW>(l, m, bias, E, k, scaling, tk, idx, gate);
+}
 
-  int pos = 0;
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const uint64_t bal = __ballot(sel[i]);
-    if (sel[i]) {
-      const int o = t * k + pos + __popcll(bal & lanemask_lt());
-      idx[o] = lane + 64 * i;
-      gate[o] = scaling * p[i];
-    }
-    pos += __popcll(bal);
+#ifndef MOE_ROUTER_WAVES
+#define MOE_ROUTER_WAVES 8
+#endif
+
+bool router_topk_fused_ok(int T, int E, int d_model, int dtype) {
+  return dtype == MOE_BF16 && E <= 128 && d_model % (128 * MOE_ROUTER_WAVES) == 0 && T >= 1;
+}
+
+int launch_router_topk(const void* x, const void* wr, const float* col_bias, float* logits_out,
+                       const float* bias, int T, int E, int d, int k, float scaling,
+                       int32_t* idx, float* gate, hipStream_t st) {
+  constexpr int NW = MOE_ROUTER_WAVES;
+  const dim3 grid((T + 15) / 16), block(64 * NW);
+#define MOE_RT(NCB)                                                                         \
+  hipLaunchKernelGGL((router_topk_kernel<NCB, NW>), grid, block, 0, st, (const __bf16*)x,    \
+                     (const __bf16*)wr, col_bias, logits_out, bias, T, E, d, k, scaling, idx, \
+                     gate)
+  switch ((E + 15) / 16) {
+    case 1: MOE_RT(1); break;
+    case 2: MOE_RT(2); break;
+    case 3: MOE_RT(3); break;
+    case 4: MOE_RT(4); break;
+    case 5: MOE_RT(5); break;
+    case 6: MOE_RT(6); break;
+    case 7: MOE_RT(7); break;
+    default: MOE_RT(8); break;
   }
+#undef MOE_RT
+  return check_launch();
 }
 
 int launch_topk(const float* partials, int nsplit, const float* col_bias, float* logits_out,

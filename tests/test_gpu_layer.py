@@ -63,6 +63,8 @@ def test_small_bf16_workload_batch0():
     (1, 64, 3, 1, 64, 2),          # single token
     (2048, 512, 16, 8, 384, 4),    # bf16: 256x256 direct-to-LDS tiles, 2 m-tiles/expert,
                                    # K-steps 8 (gate/up) and 6 (down)
+    (777, 1024, 24, 16, 256, 5),   # bf16: router + top-k in one kernel (40 experts: a
+                                   # partial 16-expert block; a partial 16-token block)
 ])
 def test_ragged_shapes(dtype, shape):
     T, d, N, Z, dff, k = shape
