@@ -9,6 +9,8 @@
 //   rows    one wave per expert: exclusive scan of the expert's row of that
 //           table (contiguous, so the reads coalesce) -> the first position
 //           of chunk b inside expert e's segment; the row total is counts[e].
+//   (up to 4096 assignments the three steps run in one workgroup instead:
+//   dispatch_one_kernel below)
 //   scatter nb blocks: each block scans counts into the expert offsets (block
 //           0 writes them out), so (expert e, chunk b) starts at
 //           offsets[e] + row prefix.  Each of the 4 waves of block b owns a
@@ -154,9 +156,93 @@ dispatch_scatter_kernel(const int32_t* __restrict__ idx, int Tk, int E,
   }
 }
 
+// The whole dispatch in one workgroup of 16 waves, for up to 4096
+// assignments (one launch instead of three).  Wave w owns the contiguous
+// chunk w of the assignments: per-wave LDS histograms, then thread e sums
+// expert e over the waves (counts), the counts are scanned into offsets and
+// each wave's first position per expert follows in wave order; then every
+// wave ranks and scatters its chunk as in dispatch_scatter_kernel.  Same
+// stable order (expert, assignment id) as the three-kernel path.
+constexpr int kDispOneWaves = 16;
+constexpr int kDispOneMax = 4096;
+
+template <int NBITS>
+__global__ void __launch_bounds__(64 * kDispOneWaves)
+dispatch_one_kernel(const int32_t* __restrict__ idx, int Tk, int E, int32_t* __restrict__ counts,
+                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+                    int32_t* __restrict__ inv_perm) {
+  extern __shared__ int s_w[];  // [kDispOneWaves][E]
+  __shared__ int s_tmp[kDispOneWaves];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int chunk = (Tk + kDispOneWaves - 1) / kDispOneWaves;
+  const int wlo = min(Tk, w * chunk), whi = min(Tk, wlo + chunk);
+
+  for (int i = threadIdx.x; i < kDispOneWaves * E; i += blockDim.x) s_w[i] = 0;
+  __syncthreads();
+  for (int a = wlo + lane; a < whi; a += 64) {
+    const int e = idx[a];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&s_w[w * E + e], 1);  // ids in range by contract
+  }
+  __syncthreads();
+  // thread e: count of expert e, then the exclusive scan over experts
+  const int e = threadIdx.x;  // E <= 1024 = blockDim.x
+  int c = 0;
+  if (e < E)
+    for (int q = 0; q < kDispOneWaves; ++q) c += s_w[q * E + e];
+  const int start = block_inclusive_scan<64 * kDispOneWaves>(c, s_tmp) - c;
+  if (e < E) {
+    counts[e] = c;
+    offsets[e] = start;
+    int run = start;
+    for (int q = 0; q < kDispOneWaves; ++q) {
+      const int v = s_w[q * E + e];
+      s_w[q * E + e] = run;
+      run += v;
+    }
+  }
+  if (threadIdx.x == 0) offsets[E] = Tk;
+  __syncthreads();
+
+  int* my = s_w + w * E;
+  for (int a0 = wlo; a0 < whi; a0 += 64) {
+    const int a = a0 + lane;
+    const int e0 = (a < whi) ? idx[a] : -1;
+    const bool valid = (unsigned)e0 < (unsigned)E;
+    const int ex = valid ? e0 : 0;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < NBITS; ++bit) {
+      const bool sb = (ex >> bit) & 1;
+      const uint64_t m = __ballot(sb);
+      peers &= sb ? m : ~m;
+    }
+    if (valid) {
+      const int rank = __popcll(peers & lanemask_lt());
+      const int pos = my[ex] + rank;
+      perm[pos] = a;
+      inv_perm[a] = pos;
+    }
+    // the highest lane of each peer group advances that expert's cursor
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (peers >> lane) == 1ull) my[ex] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 int launch_dispatch(const int32_t* idx, int Tk, int E, int nb, int32_t* block_hist,
                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
                     hipStream_t st) {
+  // 16 E ints of dynamic LDS stay under the 64 KiB default
+  if (Tk <= kDispOneMax && E <= 1000) {
+    const size_t lds = (size_t)kDispOneWaves * E * sizeof(int);
+    if (E <= 256)
+      hipLaunchKernelGGL(dispatch_one_kernel<8>, dim3(1), dim3(64 * kDispOneWaves), lds, st,
+                         idx, Tk, E, counts, offsets, perm, inv_perm);
+    else
+      hipLaunchKernelGGL(dispatch_one_kernel<10>, dim3(1), dim3(64 * kDispOneWaves), lds, st,
+                         idx, Tk, E, counts, offsets, perm, inv_perm);
+    return check_launch();
+  }
   hipLaunchKernelGGL(dispatch_hist_kernel, dim3(nb), dim3(kDispThreads), E * sizeof(int), st,
                      idx, Tk, E, block_hist);
   int rc = check_launch();
