@@ -8,8 +8,9 @@
 // (token rows) and B (weight rows) are staged in LDS as 128-byte rows per
 // K-step, with the chunk index XOR-swizzled by (row & 7) so that both the
 // row-wise global->LDS stores and the fragment reads are bank-conflict free.
-// Two LDS stages: the next K-step's global loads are in flight while the
-// current stage feeds the MFMAs.
+// Two LDS stages and two register sets: while one stage feeds the MFMAs,
+// the next K-step waits in the other stage and the global loads of the one
+// after it are in flight into registers.
 //
 // Work is a persistent loop over (group, n-tile, m-tile) tiles.  Each
 // workgroup derives the tile list itself from the group offsets, so no host

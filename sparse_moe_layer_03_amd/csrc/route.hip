@@ -1,16 +1,18 @@
-// Softmax + biased top-k + gates, one wave64 per token.
+// Router softmax, biased top-k and gates; and, for at most 128 experts in
+// bf16, the router GEMM fused with them (router_topk_kernel).
 //
 // LongCat-2.0 data sheet (archdb), table "Mixture of experts": the router
 // scores FFN and identity experts together and selects the top k by score
 // plus e_score_correction_bias; the gates are the unbiased scores times the
 // routed scaling factor, not renormalised.
 //
-// Each lane holds experts lane, lane+64, ... in registers (E <= 1024 -> at
-// most 16 per lane).  The softmax max/sum and every selection round are
-// butterfly reductions over the wave in a fixed order, so the result is
-// deterministic.  Selection compares (key, -id): larger key wins, equal keys
-// go to the lower expert id.  The chosen set is emitted in ascending expert
-// id with a ballot per register slot.
+// Selection runs in one wave64 per token, or per few tokens at once: each
+// lane holds experts lane, lane+64, ... in registers (E <= 1024 -> at most 16
+// per lane).  The softmax max/sum and every selection round are butterfly
+// reductions over the wave in a fixed order, so the result is deterministic.
+// Selection compares (key, -id): larger key wins, equal keys go to the lower
+// expert id.  The chosen set is emitted in ascending expert id with a ballot
+// per register slot.
 
 #include <math.h>
 
