@@ -14,7 +14,9 @@ GPU's selection, with the oracle's own gates.
 
 from __future__ import annotations
 
+import json
 import math
+import os
 import sys
 
 import numpy as np
@@ -165,3 +167,32 @@ def tolerances(dtype: str):
     if dtype == "bf16":
         return dict(y=1e-2, logits=1e-4, gate_rtol=1e-4)
     return dict(y=1e-5, logits=1e-5, gate_rtol=1e-5)
+
+
+# whole-layer parity ---------------------------------------------------------
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def zipf_alpha():
+    with open(os.path.join(GOLDEN, "zipf_alpha.json")) as f:
+        return json.load(f)["alpha"]
+
+
+def full_parity(w, batch=0, x_perm=False, bias=None):
+    say(f"[parity] {w}")
+    m = Model(w, "cuda", zipf_alpha() if w.zipf_s else None, bias=bias)
+    x = S.make_x(w, batch, "cuda")
+    gpu, _ = run_gpu(m, x, x_perm=x_perm)
+    tol = tolerances(w.dtype)
+    ref = oracle_route(m, x)
+    rep = {}
+    check_routing(gpu, ref, w.top_k, tol["logits"], rep)
+    check_gates(gpu, ref, w.routed_scaling, tol["gate_rtol"])
+    check_dispatch(gpu, w.E)
+    o = full_oracle(m, x, gpu_idx=gpu["topk_idx"])
+    err = row_rel_l2(gpu["y"], o["y"])
+    say(f"  uncertified={rep['uncertified']} logit_maxdiff={rep['logit_maxdiff']:.2e} "
+        f"y_row_relL2_max={err.max():.3e} mean={err.mean():.3e}")
+    assert err.max() <= tol["y"]
+    return gpu, o

@@ -2,45 +2,16 @@
 against the oracle, through the C ABI, on the workload shapes and on
 ragged multi-tile shapes."""
 
-import dataclasses
-import json
-import os
-
 import numpy as np
 import pytest
 import torch
 
 from sparse_moe_layer_03_amd import synth as S
 from tests.parity_util import (Model, check_dispatch, check_gates, check_routing,
-                               full_oracle, oracle_outputs_for_tokens, oracle_route,
-                               row_rel_l2, run_gpu, say, tolerances)
+                               full_oracle, full_parity, oracle_outputs_for_tokens,
+                               oracle_route, row_rel_l2, run_gpu, say, tolerances, zipf_alpha)
 
 pytestmark = pytest.mark.gpu
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-
-
-def zipf_alpha():
-    with open(os.path.join(GOLDEN, "zipf_alpha.json")) as f:
-        return json.load(f)["alpha"]
-
-
-def full_parity(w, batch=0, x_perm=False, bias=None):
-    say(f"[parity] {w}")
-    m = Model(w, "cuda", zipf_alpha() if w.zipf_s else None, bias=bias)
-    x = S.make_x(w, batch, "cuda")
-    gpu, _ = run_gpu(m, x, x_perm=x_perm)
-    tol = tolerances(w.dtype)
-    ref = oracle_route(m, x)
-    rep = {}
-    check_routing(gpu, ref, w.top_k, tol["logits"], rep)
-    check_gates(gpu, ref, w.routed_scaling, tol["gate_rtol"])
-    check_dispatch(gpu, w.E)
-    o = full_oracle(m, x, gpu_idx=gpu["topk_idx"])
-    err = row_rel_l2(gpu["y"], o["y"])
-    say(f"  uncertified={rep['uncertified']} logit_maxdiff={rep['logit_maxdiff']:.2e} "
-        f"y_row_relL2_max={err.max():.3e} mean={err.mean():.3e}")
-    assert err.max() <= tol["y"]
-    return gpu, o
 
 
 def test_tiny_f32_workload():
