@@ -93,8 +93,10 @@ typedef struct {
   int32_t flags;
 } moe_pid_state;
 
-/* Bytes of device scratch `ws` that the calls below need for `shape`.
- * Returns 0 if the shape is invalid. */
+/* Bytes of device scratch `ws` that the calls below need for `shape` on the
+ * current device (the router's K-split count, and with it the size, can
+ * depend on the device's multiprocessor count).  Returns 0 if the shape is
+ * invalid. */
 size_t moe_workspace_bytes(const moe_shape* shape);
 
 /* Text for a status code (static storage). */

@@ -66,6 +66,34 @@ struct WsLayout {
 };
 
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+static long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// Router GEMM plan.  The one-kernel router + top-k takes up to 128 experts.
+// Above that, many tokens go through the 256x256 kernel with its K loop
+// split so that the (split, tile) items fill about one round of the chip;
+// otherwise the general kernel (128x128 tiles, or 16-row tiles with a split
+// K loop).  The split count sizes the partial-logit workspace, so it is a
+// function of the shape and the device's CU count only.
+struct RouterPlan {
+  bool big;
+  int ksplit;
+};
+static RouterPlan router_plan(const moe_shape* s) {
+  const int E = s->n_ffn + s->n_zero;
+  const RouterPlan general{false, router_ksplit(s->T, E, s->d_model, s->dtype)};
+  if (router_topk_fused_ok(s->T, E, s->d_model, s->dtype)) return general;
+  if (s->dtype != MOE_BF16 || s->d_model % 128 != 0 || s->T < 512 ||
+      (size_t)s->T * s->d_model * 2 >= (1ull << 32) ||
+      (size_t)E * s->d_model * 2 >= (1ull << 32))
+    return general;
+  const long items = cdiv(s->T, kBigTileRows) * cdiv(E, 256);
+  const int nK = s->d_model / 64;
+  const int G = big_grid();
+  int ks = 1;
+  while (ks < 8 && items * ks * 2 <= G && nK % (4 * ks) == 0) ks *= 2;
+  if (items * ks * 2 < G) return general;  // too few tiles even when split
+  return RouterPlan{true, ks};
+}
 
 static WsLayout ws_layout(const moe_shape* s) {
   const size_t E = (size_t)s->n_ffn + s->n_zero;
@@ -73,8 +101,7 @@ static WsLayout ws_layout(const moe_shape* s) {
   WsLayout w;
   size_t off = 0;
   w.logits = off;  // K-split partial logits
-  off = up256(off + (size_t)router_ksplit(s->T, (int)E, s->d_model, s->dtype) * s->T * E *
-                        sizeof(float));
+  off = up256(off + (size_t)router_plan(s).ksplit * s->T * E * sizeof(float));
   w.hist = off;
   off = up256(off + E * (size_t)dispatch_blocks((long)Tk) * sizeof(int32_t));
   w.h = off;
@@ -87,7 +114,6 @@ static WsLayout ws_layout(const moe_shape* s) {
 // make tall tiles worth it, but only if there are enough of them to spread
 // over the chip: a dense batch of 128 rows through one expert (T*k/E = 128)
 // gives a single row of tiles, so 16-row tiles are used for it.
-static long cdiv(long a, long b) { return (a + b - 1) / b; }
 static constexpr long kMinTiles = 64;
 
 // 128x128 tiles (else 16x128) for the general kernel.
@@ -163,7 +189,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
   if (router_topk_fused_ok(s->T, E, s->d_model, s->dtype))
     return launch_router_topk(x, w_router, logit_bias, logits_out, bias, s->T, E, s->d_model,
                               s->top_k, s->routed_scaling, topk_idx, topk_gate, st);
-  const int nsplit = router_ksplit(s->T, E, s->d_model, s->dtype);
+  const RouterPlan plan = router_plan(s);
+  const int nsplit = plan.ksplit;
   float* partials = (float*)((char*)ws + ws_layout(s).logits);
   GemmArgs g{};
   g.a = x;
@@ -175,7 +202,7 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
   g.ngroups = 1;
   g.top_k = s->top_k;
   g.ksplit = nsplit;
-  rc = launch_gemm(s->dtype, 0, router_big_tiles(s), g, st);
+  rc = plan.big ? launch_gemm_big(0, g, st) : launch_gemm(s->dtype, 0, router_big_tiles(s), g, st);
   if (rc) return rc;
   return launch_topk(partials, nsplit, logit_bias, logits_out, bias, s->T, E, s->top_k,
                      s->routed_scaling, topk_idx, topk_gate, st);

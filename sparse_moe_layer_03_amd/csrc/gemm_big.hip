@@ -1,5 +1,8 @@
 // Grouped bf16 expert GEMMs for batches with many rows per expert (prefill-
 // shaped and skewed batches): gate/up with a fused SwiGLU epilogue, and down.
+// The same kernel (mode 0) runs the router GEMM of a many-token batch with
+// more than 128 experts: one group of T rows, fp32 partial logits, its K
+// loop split into ksplit ranges so that (split, tile) items fill the chip.
 //
 // Built around what gfx950 executes fastest:
 //  * v_mfma_f32_32x32x16_bf16: one wave keeps the matrix pipe busy with only
@@ -109,7 +112,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
     for (int i = 0; i < PER; ++i) {
       const int gi = tid * PER + i;
       int mt = 0;
-      if (gi < ngroups) mt = (g.offsets[gi + 1] - g.offsets[gi] + BM - 1) / BM;
+      if (gi < ngroups)
+        mt = ((MODE == 0 ? g.M : g.offsets[gi + 1] - g.offsets[gi]) + BM - 1) / BM;
       run += mt;
       loc[i] = run;
     }
@@ -123,9 +127,13 @@ grouped_gemm_big_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
-  const int total = s_pref[ngroups] * ntiles;
+  // the router (mode 0) splits its K loop: work item t is split t / tiles
+  // of tile t % tiles, so the tiles running together share a K range
+  const int ksplit = (MODE == 0) ? g.ksplit : 1;
+  const int tiles = s_pref[ngroups] * ntiles;
+  const int total = tiles * ksplit;
   auto find = [&](int t) -> uint32_t {  // (first m-tile << 10) | group
-    if (t >= total) return 0;
+    if (t >= tiles) return 0;
     const int m = t / ntiles;
     int lo = 0, hi = ngroups - 1;  // last group with s_pref[grp] <= m
     while (lo < hi) {
@@ -134,10 +142,10 @@ grouped_gemm_big_kernel(GemmArgs g) {
     }
     return ((uint32_t)s_pref[lo] << 10) | (uint32_t)lo;
   };
-  const uint32_t tdesc0 = find(vid + lane * G);
-  const uint32_t tdesc1 = find(vid + (64 + lane) * G);
+  const uint32_t tdesc0 = (MODE == 0) ? 0u : find(vid + lane * G);
+  const uint32_t tdesc1 = (MODE == 0) ? 0u : find(vid + (64 + lane) * G);
   __syncthreads();  // the prefix is dead before the first DMA into s_a0
-  const int nK = g.K / KS;  // the host guarantees an even count
+  const int nK = g.K / KS / ksplit;  // per split; the host guarantees an even count
   const size_t row_bytes = (size_t)g.K * 2;
 
   // DMA lane geometry: lane fills slot (lane % 8) of row (lane / 8) of a KiB
@@ -147,12 +155,13 @@ grouped_gemm_big_kernel(GemmArgs g) {
   const int dma_slot = lane % 8;
 
   for (int k = 0; vid + k * G < total; ++k) {
-    const int t = vid + k * G;
+    const int tsplit = (MODE == 0) ? (vid + k * G) / tiles : 0;
+    const int t = vid + k * G - tsplit * tiles;
     const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(
         (int)(k < 64 ? tdesc0 : tdesc1), k & 63);
-    const int grp = (int)(d & 1023u);
-    const int tp0 = (int)(d >> 10);
-    const int cnt_g = g.offsets[grp + 1] - g.offsets[grp];
+    const int grp = (MODE == 0) ? 0 : (int)(d & 1023u);
+    const int tp0 = (MODE == 0) ? 0 : (int)(d >> 10);
+    const int cnt_g = (MODE == 0) ? g.M : g.offsets[grp + 1] - g.offsets[grp];
     const int mt_g = (cnt_g + BM - 1) / BM;
     const int local = t - tp0 * ntiles;
     // Within an expert, tiles go in groups of MG m-tiles x all n-tiles (n-tile
@@ -162,8 +171,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int mg = min(MG, mt_g - grp_m0);
     const int in_grp = local - grp_m0 * ntiles;
     const int nt = in_grp / mg, mi = grp_m0 + in_grp % mg;
-    const int row0 = g.offsets[grp];
-    const int cnt = g.offsets[grp + 1] - row0;
+    const int row0 = (MODE == 0) ? 0 : g.offsets[grp];
+    const int cnt = cnt_g;
     const int h = ((cnt + mt_g - 1) / mt_g + 31) & ~31;  // balanced tile height
     const int m0 = mi * h;
     const int m_end = min(cnt, m0 + h);                  // rows [m0, m_end)
@@ -172,7 +181,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int nrb = (m_end - m0 + 31) / 32;
     const int mba = min(MB, (nrb - wm + WM - 1) / WM);
 
-    // ---- per-lane DMA source offsets (32-bit; bases are wave-uniform)
+    // ---- per-lane DMA source offsets (32-bit; bases are wave-uniform),
+    // starting at this split's K range
+    const uint32_t k_base = (uint32_t)(tsplit * nK * RB);
     const char* a_base = (const char*)g.a;
     uint32_t a_off[A_PW];
 #pragma unroll
@@ -187,7 +198,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       } else {
         src_row = row0 + rr;
       }
-      a_off[q] = (uint32_t)(src_row * row_bytes) + swz(r, dma_slot) * 16;
+      a_off[q] = (uint32_t)(src_row * row_bytes) + k_base + swz(r, dma_slot) * 16;
     }
     const char* b_base0 = (const char*)g.b0 + (size_t)grp * g.N * row_bytes;
     const char* b_base1 =
@@ -198,7 +209,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       const int r = (wave + q * NW) * RPK + dma_row;
       int n = (MODE == 1 && r >= HN) ? n0 + r - HN : n0 + r;
       if (n > g.N - 1) n = g.N - 1;
-      b_off[q] = (uint32_t)(n * row_bytes) + swz(r, dma_slot) * 16;
+      b_off[q] = (uint32_t)(n * row_bytes) + k_base + swz(r, dma_slot) * 16;
     }
 
     f32x16_t acc[MB][NB];
@@ -387,9 +398,25 @@ grouped_gemm_big_kernel(GemmArgs g) {
       const int r = m0 + (i * WM + wm) * 32 + r32;
       if (r < m_end) {
         char* crow = (char*)g.c + (size_t)(row0 + r) * g.N * 2;
+        float* prow = (float*)g.c + ((size_t)tsplit * g.M + r) * g.N;  // mode 0
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (MODE == 1) {
+          if (MODE == 0) {
+            // fp32 partial logits of this K split, [split][T][E]
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              const int col = n0 + wn * WTN + j * 32 + 8 * q + 4 * kg;
+              if ((g.N & 3) == 0 && col + 3 < g.N) {
+                *reinterpret_cast<float4*>(prow + col) =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (col + e < g.N) prow[col + e] = acc[i][j][4 * q + e];
+              }
+            }
+          } else if (MODE == 1) {
 #pragma unroll
             for (int j = 0; j < NB / 2; ++j) {
               const int col = n0 + wn * (WTN / 2) + j * 32 + 8 * q + 4 * kg;
@@ -449,6 +476,11 @@ static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
 
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
   if (g.K % 128 != 0 || g.ngroups < 1 || g.ngroups > kBigMaxGroups) return MOE_EINVAL;
+  if (mode == 0) {
+    // each split covers an even number (>= 2) of 64-wide K-steps
+    if (g.ngroups != 1 || g.ksplit < 1 || (g.K / 64) % (2 * g.ksplit) != 0) return MOE_EINVAL;
+    return launch_big_mode<0>(g, st);
+  }
   return mode == 1 ? launch_big_mode<1>(g, st) : launch_big_mode<2>(g, st);
 }
 

@@ -3,7 +3,10 @@
 moe_route runs the router GEMM and the top-k in one kernel for bf16 with at
 most 128 experts and d_model a multiple of 1024; that kernel works in 16-expert
 column blocks (1 to 8 of them) and keeps four 32-wide K-steps in flight per
-wave.  moe_dispatch sorts in one workgroup for at most 4096 assignments and
+wave.  Above 128 experts, a batch of many tokens runs the router GEMM in 256x256
+tiles with its K loop split so that one round fills the chip (fp32 partial
+logits per split, summed in split order by the top-k kernel).
+moe_dispatch sorts in one workgroup for at most 4096 assignments and
 1000 experts, and in a histogram / row-scan / scatter sequence otherwise.
 moe_combine holds up to 8 slots per token in one variant and up to 16 in the
 other.  Each case below sits on one side of such a limit and is checked
@@ -40,4 +43,15 @@ def test_fused_router_column_blocks_and_k_steps(T, N, Z, k, d):
 def test_dispatch_at_the_one_workgroup_limit(T, N, Z, k):
     w = S.Workload("dispatch_limit", T=T, d_model=64, n_ffn=N, n_zero=Z, d_ff=64, top_k=k,
                    dtype="f32", bias_var=0.01, seed=22)
+    full_parity(w)
+
+
+@pytest.mark.parametrize("T,N,Z,k,d", [
+    (4000, 200, 100, 6, 1536),   # 300 experts: K split 4, a partial n-tile, E not a multiple of 4
+    (2048, 384, 128, 8, 1024),   # 512 experts: K split 8, two 64-wide K-steps per split
+    (12000, 512, 256, 2, 512),   # 768 experts: no split, last m-tile of 224 rows
+])
+def test_router_many_tokens_split_k(T, N, Z, k, d):
+    w = S.Workload("router_big", T=T, d_model=d, n_ffn=N, n_zero=Z, d_ff=64, top_k=k,
+                   dtype="bf16", bias_var=0.01, seed=23)
     full_parity(w)
