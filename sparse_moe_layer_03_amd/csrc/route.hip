@@ -8,11 +8,13 @@
 //
 // Selection runs in one wave64 per token, or per few tokens at once: each
 // lane holds experts lane, lane+64, ... in registers (E <= 1024 -> at most 16
-// per lane).  The softmax max/sum and every selection round are butterfly
-// reductions over the wave in a fixed order, so the result is deterministic.
-// Selection compares (key, -id): larger key wins, equal keys go to the lower
-// expert id.  The chosen set is emitted in ascending expert id with a ballot
-// per register slot.
+// per lane).  The softmax max and sum are butterfly reductions over the wave
+// in a fixed order, so the result is deterministic.  The top k are found by
+// a radix select on the fp32 keys mapped to order-preserving integers: the
+// k-th largest key is built bit by bit with ballot counts, then every key
+// above it and the keys equal to it in ascending expert id are taken (larger
+// key wins, equal keys go to the lower expert id).  The chosen set is
+// emitted in ascending expert id with a ballot per register slot.
 
 #include <math.h>
 
@@ -52,58 +54,59 @@ __device__ __forceinline__ void select_topk(float (&l)[NT][PL], float (&m)[NT],
   for (int o = 32; o > 0; o >>= 1)
 #pragma unroll
     for (int n = 0; n < NT; ++n) s[n] += __shfl_xor(s[n], o, kWave);
-  float key[NT][PL];
-  bool avail[NT][PL], sel[NT][PL];
+  // Selection key p + bias in fp32, mapped to an unsigned integer with the
+  // same order (NaN ranks as -inf, -0 as +0); experts past E map to 0,
+  // below every real key.
+  uint32_t u[NT][PL];
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int e = lane + 64 * i;
       p[n][i] = p[n][i] / s[n];
-      avail[n][i] = e < E;
-      sel[n][i] = false;
-      key[n][i] = avail[n][i] ? p[n][i] + bias[e] : 0.f;
-      if (key[n][i] != key[n][i]) key[n][i] = -INFINITY;  // NaN never outranks a number
+      if (e < E) {
+        float key = p[n][i] + bias[e];
+        if (key != key) key = -INFINITY;
+        key += 0.0f;  // -0 -> +0
+        const uint32_t b = __float_as_uint(key);
+        u[n][i] = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+      } else {
+        u[n][i] = 0u;
+      }
     }
-
-  for (int r = 0; r < k; ++r) {
-    float bk[NT];
-    int bid[NT];
+  // The k-th largest mapped key, found bit by bit from the top: keep bit b
+  // if at least k keys are >= the threshold with it set.  Counts are wave
+  // ballots, so no lane exchanges data.
+  uint32_t thr[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) thr[n] = 0u;
+  for (int b = 31; b >= 0; --b) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      bk[n] = -INFINITY;
-      bid[n] = 0x7fffffff;
+      const uint32_t cand = thr[n] | (1u << b);
+      int cnt = 0;
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const int e = lane + 64 * i;
-        if (avail[n][i] && (key[n][i] > bk[n] || (key[n][i] == bk[n] && e < bid[n]))) {
-          bk[n] = key[n][i];
-          bid[n] = e;
-        }
-      }
+      for (int i = 0; i < PL; ++i) cnt += __popcll(__ballot(u[n][i] >= cand));
+      if (cnt >= k) thr[n] = cand;
     }
+  }
+  // Selected: every key above the threshold, then the keys equal to it in
+  // ascending expert id (slot i holds ids 64 i + lane) until k are chosen.
+  bool sel[NT][PL];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
+  for (int n = 0; n < NT; ++n) {
+    int above = 0;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const float ok = __shfl_xor(bk[n], o, kWave);
-        const int oid = __shfl_xor(bid[n], o, kWave);
-        if (ok > bk[n] || (ok == bk[n] && oid < bid[n])) {
-          bk[n] = ok;
-          bid[n] = oid;
-        }
-      }
+    for (int i = 0; i < PL; ++i) above += __popcll(__ballot(u[n][i] > thr[n]));
+    int ties_before = 0;
+    const int need = k - above;  // >= 1
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const uint64_t tie = __ballot(u[n][i] == thr[n]);
+      const int rank = ties_before + __popcll(tie & lanemask_lt());
+      sel[n][i] = u[n][i] > thr[n] || (u[n][i] == thr[n] && rank < need);
+      ties_before += __popcll(tie);
     }
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-      if ((bid[n] & 63) == lane) {
-#pragma unroll
-        for (int i = 0; i < PL; ++i)
-          if (i == (bid[n] >> 6)) {
-            avail[n][i] = false;
-            sel[n][i] = true;
-          }
-      }
   }
 
 #pragma unroll
@@ -135,15 +138,25 @@ topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restr
   float l[PL];
   float m = -INFINITY;
   if constexpr (U == 1) {
+    // the PL loads of a split are independent (issued together, one
+    // latency); the splits are added in order
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane + 64 * i;
+      l[i] = e < E ? partials[(size_t)t * E + e] : 0.f;
+    }
+    for (int sp = 1; sp < nsplit; ++sp)
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) l[i] += partials[((size_t)sp * T + t) * E + e];
+      }
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int e = lane + 64 * i;
       if (e < E) {
-        float v = partials[(size_t)t * E + e];
-        for (int sp = 1; sp < nsplit; ++sp) v += partials[((size_t)sp * T + t) * E + e];
-        if (col_bias != nullptr) v += col_bias[e];
-        if (logits_out != nullptr) logits_out[(size_t)t * E + e] = v;
-        l[i] = v;
+        if (col_bias != nullptr) l[i] += col_bias[e];
+        if (logits_out != nullptr) logits_out[(size_t)t * E + e] = l[i];
       } else {
         l[i] = -INFINITY;
       }
