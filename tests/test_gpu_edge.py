@@ -1,6 +1,7 @@
 """GPU edge cases: identity-only routing, dense mixture (k = E, no zero
-experts), the largest expert count and k, infinite biases, determinism and
-the FFN stage fed from oracle-made dispatch arrays."""
+experts), the largest expert count and k, infinite biases, determinism, the
+FFN stage fed from oracle-made dispatch arrays, and exact ties at the top-k
+boundary."""
 
 import numpy as np
 import pytest
@@ -103,3 +104,24 @@ def test_ffn_stage_with_oracle_dispatch_arrays():
     n = int(ref["offsets"][w.n_ffn])
     assert row_rel_l2(S.to_numpy64(buf.y_perm[:n]), ref["y_perm"]).max() <= 1e-5
     assert row_rel_l2(S.to_numpy64(buf.y), ref["y"]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype,d,N,Z,k", [
+    ("bf16", 1024, 80, 40, 8),    # router and top-k in one kernel
+    ("f32", 128, 200, 100, 12),   # top-k kernel, 5 experts per lane
+    ("bf16", 256, 700, 300, 16),  # top-k kernel, 16 experts per lane
+])
+def test_exact_ties_pick_lowest_ids(dtype, d, N, Z, k):
+    # A zero router matrix makes every score exactly 1/E; the bias repeats
+    # a few values, so the k-th key is tied across many experts and the
+    # lowest ids among the ties must be taken.
+    w = S.Workload("ties", T=70, d_model=d, n_ffn=N, n_zero=Z, d_ff=64, top_k=k, dtype=dtype,
+                   seed=9)
+    bias = np.array([(0.25, 0.0, 0.25, -0.5, 0.0)[e % 5] for e in range(w.E)], np.float32)
+    m = Model(w, "cuda", bias=bias)
+    m.wr.zero_()
+    x = S.make_x(w, 0, "cuda")
+    gpu, _ = run_gpu(m, x)
+    ref = O.route(S.to_numpy64(x), np.zeros((w.E, d)), bias, k, w.routed_scaling)
+    np.testing.assert_array_equal(gpu["topk_idx"], ref["topk_idx"])
+    check_dispatch(gpu, w.E)
