@@ -100,8 +100,9 @@ static WsLayout ws_layout(const moe_shape* s) {
   const size_t Tk = (size_t)s->T * s->top_k;
   WsLayout w;
   size_t off = 0;
-  w.logits = off;  // K-split partial logits
-  off = up256(off + (size_t)router_plan(s).ksplit * s->T * E * sizeof(float));
+  w.logits = off;  // K-split partial logits, then slack: the top-k kernel
+                   // reads whole 64-expert slots of the last row
+  off = up256(off + (size_t)router_plan(s).ksplit * s->T * E * sizeof(float) + 4096);
   w.hist = off;
   off = up256(off + E * (size_t)dispatch_blocks((long)Tk) * sizeof(int32_t));
   w.h = off;

@@ -24,7 +24,8 @@
 namespace moe {
 
 // Softmax, biased top-k and gates of NT tokens held by one wave (lane holds
-// experts lane + 64 i of each; m[n] is the lane's partial max of token n);
+// experts lane + 64 i of each; m[n] is the lane's partial max of token n;
+// bias must be readable at [0, 64 PL), e.g. a copy in LDS padded past E);
 // writes token t[n]'s k slots of idx / gate in ascending expert id, for the
 // tokens with t[n] >= 0.  The NT tokens' reductions are independent chains
 // interleaved step by step, so their shuffle latencies overlap.
@@ -64,8 +65,9 @@ __device__ __forceinline__ void select_topk(float (&l)[NT][PL], float (&m)[NT],
     for (int i = 0; i < PL; ++i) {
       const int e = lane + 64 * i;
       p[n][i] = p[n][i] / s[n];
+      const float bv = bias[lane + 64 * i];  // readable for every slot
       if (e < E) {
-        float key = p[n][i] + bias[e];
+        float key = p[n][i] + bv;
         if (key != key) key = -INFINITY;
         key += 0.0f;  // -0 -> +0
         const uint32_t b = __float_as_uint(key);
@@ -130,55 +132,40 @@ __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restrict__ col_bias,
             float* __restrict__ logits_out, const float* __restrict__ bias, int T, int E,
             int k, float scaling, int32_t* __restrict__ idx, float* __restrict__ gate) {
+  // selection bias and classifier offset in LDS, zero past E, so every slot
+  // reads them unconditionally
+  __shared__ float s_bias[64 * PL], s_cb[64 * PL];
+  for (int e = threadIdx.x; e < 64 * PL; e += blockDim.x) {
+    s_bias[e] = e < E ? bias[e] : 0.f;
+    s_cb[e] = (col_bias != nullptr && e < E) ? col_bias[e] : 0.f;
+  }
+  __syncthreads();
   const int lane = lane_id();
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform per wave
 
-  // logits = sum of the K-split partials in split order (+ classifier offset)
+  // logits = sum of the K-split partials ([split][T][E]) in split order.  A
+  // lane reads experts lane + 64 i of its row for every slot: the slots past
+  // E read into the next row or, for the last row, into the workspace's
+  // slack, and are discarded below.
+  const float* row = partials + (size_t)t * E + lane;
+  const size_t sstride = (size_t)T * E;
   float l[PL];
-  float m = -INFINITY;
-  if constexpr (U == 1) {
-    // the PL loads of a split are independent (issued together, one
-    // latency); the splits are added in order
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = lane + 64 * i;
-      l[i] = e < E ? partials[(size_t)t * E + e] : 0.f;
-    }
+  for (int i = 0; i < PL; ++i) l[i] = row[64 * i];
+  if constexpr (U == 1) {
     for (int sp = 1; sp < nsplit; ++sp)
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E) l[i] += partials[((size_t)sp * T + t) * E + e];
-      }
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) {
-        if (col_bias != nullptr) l[i] += col_bias[e];
-        if (logits_out != nullptr) logits_out[(size_t)t * E + e] = l[i];
-      } else {
-        l[i] = -INFINITY;
-      }
-      m = fmaxf(m, l[i]);
-    }
+      for (int i = 0; i < PL; ++i) l[i] += row[sp * sstride + 64 * i];
   } else {
     // many splits and few tokens: read U splits at a time so the loads overlap
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = lane + 64 * i;
-      l[i] = e < E ? partials[(size_t)t * E + e] : 0.f;
-    }
     int sp = 1;
     for (; sp + U <= nsplit; sp += U) {
       float v[U][PL];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int i = 0; i < PL; ++i) {
-          const int e = lane + 64 * i;
-          v[u][i] = e < E ? partials[((size_t)(sp + u) * T + t) * E + e] : 0.f;
-        }
+        for (int i = 0; i < PL; ++i) v[u][i] = row[(sp + u) * sstride + 64 * i];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -186,27 +173,25 @@ topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restr
     }
     for (; sp < nsplit; ++sp)
 #pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E) l[i] += partials[((size_t)sp * T + t) * E + e];
-      }
+      for (int i = 0; i < PL; ++i) l[i] += row[sp * sstride + 64 * i];
+  }
+  float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) {
-        if (col_bias != nullptr) l[i] += col_bias[e];
-        if (logits_out != nullptr) logits_out[(size_t)t * E + e] = l[i];
-      } else {
-        l[i] = -INFINITY;
-      }
-      m = fmaxf(m, l[i]);
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + 64 * i;
+    l[i] += s_cb[e];  // + 0 without a classifier offset
+    if (e < E) {
+      if (logits_out != nullptr) logits_out[(size_t)t * E + e] = l[i];
+    } else {
+      l[i] = -INFINITY;
     }
+    m = fmaxf(m, l[i]);
   }
   float l1[1][PL], m1[1] = {m};
 #pragma unroll
   for (int i = 0; i < PL; ++i) l1[0][i] = l[i];
   const int t1[1] = {t};
-  select_topk<PL, 1>(l1, m1, bias, E, k, scaling, t1, idx, gate);
+  select_topk<PL, 1>(l1, m1, s_bias, E, k, scaling, t1, idx, gate);
 }
 
 // Router GEMM and top-k in one launch, for at most 128 experts in bf16
@@ -232,9 +217,11 @@ router_topk_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ wr,
   constexpr int LDP = NCB * 16 + 4; // LDS row pitch (floats): conflict-free stores
   static_assert(BT % NW == 0, "tokens per wave");
   __shared__ float s_part[NW][BT][LDP];
+  __shared__ float s_bias[64 * PL];  // selection bias, zero past E
   typedef float f32x4 __attribute__((ext_vector_type(4)));
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < 64 * PL; e += 64 * NW) s_bias[e] = e < E ? bias[e] : 0.f;
   const int t0 = blockIdx.x * BT;
   const int r16 = lane & 15, oct = lane >> 4;  // operand row / col, K octet
   const int kq = d / NW;                       // K per wave
@@ -308,7 +295,7 @@ router_topk_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ wr,
       m[q] = fmaxf(m[q], l[q][i]);
     }
   }
-  select_topk<PL, TPW>(l, m, bias, E, k, scaling, tk, idx, gate);
+  select_topk<PL, TPW>(l, m, s_bias, E, k, scaling, tk, idx, gate);
 }
 
 #ifndef MOE_ROUTER_WAVES
