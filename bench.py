@@ -13,8 +13,14 @@ PID set point 6 real experts/token (Kp=0.01, Ki=0.001, Kd=0) updated after
 every batch; the timed steps are batches 0..K-1 of that run, starting from
 the initial bias (warm-up steps run first and are then undone).
 
-The timed steps record three HIP events each (step start, gate/up start and
-end: each record costs GPU time).  After them, outside the timed region, the
+The steps are timed twice over the same batches and controller trajectory:
+issued one call at a time with three HIP events each (step start, gate/up
+start and end, for the step spread and the gate/up duration of the
+roofline), and as one HIP graph per step, captured once and replayed (no
+events inside).  `value` and `ms_per_step` come from the run named by
+--launch (default: graph); both runs are reported, and the graph run's final
+output and bias must equal the eager run's bit for bit.  After them, outside
+the timed region, the
 same steps are replayed once with an event at every stage boundary
 (stages_ms_mean) and every step's expert loads logged (exact assignments and
 touched experts per step for the roofline, load variance per batch), and,
@@ -49,6 +55,10 @@ def parse():
                     choices=["small_bf16", "decode_bf16", "prefill_bf16", "skewed_bf16",
                              "tiny_f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph",
+                    help="how the timed steps whose time gives `value` are launched: each "
+                         "step captured once as a HIP graph and replayed (default), or the "
+                         "library calls issued one by one; both are run and reported")
     ap.add_argument("--scmoe", type=int, default=0, metavar="D_FF",
                     help="shortcut-connected block: time the MoE layer against a dense "
                          "SwiGLU branch of this width on a second stream (e.g. 12288); "
@@ -334,6 +344,35 @@ def main():
         r_log.zero_()
         torch.cuda.synchronize()
 
+    # ---- the same K steps as HIP graphs: each step (its batch differs) is
+    # captured once, the controller is reset, all graphs are replayed once
+    # untimed and once timed.  Same kernels, same launches, same inputs and
+    # controller trajectory: the final output and bias must equal the eager
+    # run's bit for bit.
+    y_eager, bias_eager = buf.y.clone(), bias.clone()
+    graphs = []
+    cap = torch.cuda.Stream()  # default priority
+    for i in range(K):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            step(i)
+        graphs.append(gr)
+    for rep_i in range(2):
+        reset_controller()
+        g0 = time.perf_counter()
+        for gr in graphs:
+            gr.replay()
+        torch.cuda.synchronize()
+        g_elapsed = time.perf_counter() - g0
+    graph_match = bool(torch.equal(buf.y, y_eager) and torch.equal(bias, bias_eager))
+    if not graph_match:
+        print("bench.py: graph replay differs from the eager run", file=sys.stderr)
+        sys.exit(1)
+    del graphs
+    eager_elapsed = elapsed
+    if args.launch == "graph":
+        elapsed = g_elapsed
+
     # ---- untimed replay of the same K steps (same inputs, same controller
     # trajectory) with an event at every stage boundary and each step's
     # expert loads logged: the stage breakdown and exact per-step A and U
@@ -408,6 +447,11 @@ def main():
         "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
                     "p90": float(np.percentile(step_ms, 90))},
         "stages_ms_mean": {n: float(np.mean(v)) for n, v in st_ms.items()},
+        "launch": args.launch,
+        "graph": {"tokens_per_s": w.T * K / g_elapsed, "ms_per_step": g_elapsed / K * 1e3,
+                  "matches_eager": graph_match},
+        "eager": {"tokens_per_s": w.T * K / eager_elapsed,
+                  "ms_per_step": eager_elapsed / K * 1e3},
         "ffn_assignments_per_step_mean": float(np.mean(A)),
         "touched_ffn_experts_per_step_mean": float(np.mean(U)),
     }
