@@ -131,7 +131,15 @@ grouped_gemm_big_kernel(GemmArgs g) {
   // of tile t % tiles, so the tiles running together share a K range
   const int ksplit = (MODE == 0) ? g.ksplit : 1;
   const int tiles = s_pref[ngroups] * ntiles;
-  const int total = tiles * ksplit;
+  // Tail split (expert modes): when the last round of the persistent grid
+  // is at most half full, each of its tiles is cut into f row slices, so
+  // the slices spread over the idle CUs.  Items below `full` are whole
+  // tiles; item full + j is slice j % f of tile full + j / f.
+  const int full = tiles - tiles % G;
+  const int rem = tiles - full;
+  const int f = (MODE != 0 && rem > 0 && 2 * rem <= G) ? min(8, G / rem) : 1;
+  const int total = (full + rem * f) * ksplit;
+  auto tile_of = [&](int it) { return it < full ? it : full + (it - full) / f; };
   auto find = [&](int t) -> uint32_t {  // (first m-tile << 10) | group
     if (t >= tiles) return 0;
     const int m = t / ntiles;
@@ -142,8 +150,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
     }
     return ((uint32_t)s_pref[lo] << 10) | (uint32_t)lo;
   };
-  const uint32_t tdesc0 = (MODE == 0) ? 0u : find(vid + lane * G);
-  const uint32_t tdesc1 = (MODE == 0) ? 0u : find(vid + (64 + lane) * G);
+  const uint32_t tdesc0 = (MODE == 0) ? 0u : find(tile_of(vid + lane * G));
+  const uint32_t tdesc1 = (MODE == 0) ? 0u : find(tile_of(vid + (64 + lane) * G));
   __syncthreads();  // the prefix is dead before the first DMA into s_a0
   const int nK = g.K / KS / ksplit;  // per split; the host guarantees an even count
   const size_t row_bytes = (size_t)g.K * 2;
@@ -156,7 +164,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
 
   for (int k = 0; vid + k * G < total; ++k) {
     const int tsplit = (MODE == 0) ? (vid + k * G) / tiles : 0;
-    const int t = vid + k * G - tsplit * tiles;
+    const int it = vid + k * G - tsplit * tiles;  // item (== tile unless sliced)
+    const int t = tile_of(it);
     const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(
         (int)(k < 64 ? tdesc0 : tdesc1), k & 63);
     const int grp = (MODE == 0) ? 0 : (int)(d & 1023u);
@@ -174,8 +183,17 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int row0 = (MODE == 0) ? 0 : g.offsets[grp];
     const int cnt = cnt_g;
     const int h = ((cnt + mt_g - 1) / mt_g + 31) & ~31;  // balanced tile height
-    const int m0 = mi * h;
-    const int m_end = min(cnt, m0 + h);                  // rows [m0, m_end)
+    int m0 = mi * h;
+    int m_end = min(cnt, m0 + h);                        // rows [m0, m_end)
+    if (it >= full && f > 1) {
+      // slice (it - full) % f of the tile: at least 32 rows each; an empty
+      // slice (short tile) is skipped by the whole workgroup
+      const int hs = max(32, ((m_end - m0 + f - 1) / f + 31) & ~31);
+      const int s0 = m0 + ((it - full) % f) * hs;
+      m_end = min(m_end, s0 + hs);
+      m0 = s0;
+      if (m0 >= m_end) continue;
+    }
     const int n0 = nt * HN;
     // 32-row blocks of this wave that hold rows: i with (i*WM + wm)*32 < rows
     const int nrb = (m_end - m0 + 31) / 32;

@@ -9,7 +9,8 @@ logits per split, summed in split order by the top-k kernel).
 moe_dispatch sorts in one workgroup for at most 4096 assignments and
 1000 experts, and in a histogram / row-scan / scatter sequence otherwise.
 moe_combine holds up to 8 slots per token in one variant and up to 16 in the
-other.  Each case below sits on one side of such a limit and is checked
+other.  The 256x256 expert kernel cuts the tiles of a last round that is at
+most half full into f = min(8, CUs / tiles left) row slices.  Each case below sits on one side of such a limit and is checked
 against the oracle like every other layer test: routing under the
 certification rule, dispatch arrays bit-exact, outputs within tolerance."""
 
@@ -54,4 +55,14 @@ def test_dispatch_at_the_one_workgroup_limit(T, N, Z, k):
 def test_router_many_tokens_split_k(T, N, Z, k, d):
     w = S.Workload("router_big", T=T, d_model=d, n_ffn=N, n_zero=Z, d_ff=64, top_k=k,
                    dtype="bf16", bias_var=0.01, seed=23)
+    full_parity(w)
+
+
+@pytest.mark.parametrize("T,N,Z,k", [
+    (4096, 8, 4, 2),   # 28 tiles per GEMM: the only round is cut into 32-row slices (f = 8)
+    (3000, 6, 2, 3),   # 50 tiles: f = 5
+])
+def test_expert_gemm_tail_round_slices(T, N, Z, k):
+    w = S.Workload("tail_slices", T=T, d_model=512, n_ffn=N, n_zero=Z, d_ff=256, top_k=k,
+                   dtype="bf16", bias_var=0.01, seed=24)
     full_parity(w)
