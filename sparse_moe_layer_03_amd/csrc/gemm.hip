@@ -64,6 +64,11 @@ grouped_gemm_kernel(GemmArgs g) {
 
   __shared__ __attribute__((aligned(16))) char s_a[2][BM * 128];
   __shared__ __attribute__((aligned(16))) char s_b[2][BN * 128];
+  // chunks that threads past a tile's chunk count load but never use land
+  // here, so every thread stores unconditionally (no branch around the
+  // stores, which would make the compiler drain the loads in flight)
+  constexpr bool A_SPARE = A_IT * NT > A_CH, B_SPARE = B_IT * NT > B_CH;
+  __shared__ __attribute__((aligned(16))) char s_junk[(A_SPARE || B_SPARE) ? NT * 16 : 16];
   __shared__ int s_mt[kMaxGroups + 1];
   __shared__ int s_tmp[NT / 64];
 
@@ -145,7 +150,7 @@ grouped_gemm_kernel(GemmArgs g) {
       if (rr > rows - 1) rr = rows - 1;  // ragged tail: reload a valid row
       long src_row;
       if (q >= A_CH)
-        src_row = row0;
+        src_row = 0;  // a thread past the tile loads row 0 (valid in every mode), never stored
       else if (MODE == MODE_GATE_UP && g.perm != nullptr)
       {
         src_row = g.perm[row0 + rr] / g.top_k;  // gather token rows on load
@@ -153,7 +158,7 @@ grouped_gemm_kernel(GemmArgs g) {
       }
       else
         src_row = row0 + rr;
-      a_src[it] = (q < A_CH) ? (const char*)g.a + src_row * a_row_bytes + c * 16 : nullptr;
+      a_src[it] = (const char*)g.a + src_row * a_row_bytes + c * 16;
       a_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
     }
 #pragma unroll
@@ -172,7 +177,7 @@ grouped_gemm_kernel(GemmArgs g) {
         if (n > g.N - 1) n = g.N - 1;
         base = (const char*)g.b0 + (MODE == MODE_DOWN ? (size_t)grp * g.N * a_row_bytes : 0);
       }
-      b_src[it] = (q < B_CH) ? base + (size_t)n * a_row_bytes + c * 16 : nullptr;
+      b_src[it] = base + (size_t)n * a_row_bytes + c * 16;  // q >= B_CH: loaded, not stored
       b_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
     }
 
@@ -184,23 +189,28 @@ grouped_gemm_kernel(GemmArgs g) {
 
     // Two register sets carry the global loads of the next two K-steps, so a
     // load has two K-steps of MFMA work to arrive before it is written to LDS.
+    // Every thread loads every step (steps past the end repeat the last one,
+    // threads past the tile's chunks repeat a valid chunk): a load under a
+    // condition makes the compiler drain all loads in flight at that point.
     u32x4_t ra0[A_IT], rb0[B_IT], ra1[A_IT], rb1[B_IT];
     auto gload = [&](u32x4_t* ra, u32x4_t* rb, int ks) {
-      const size_t off = k_off + (size_t)ks * 128;
+      const size_t off = k_off + (size_t)min(ks, nK - 1) * 128;
 #pragma unroll
-      for (int it = 0; it < A_IT; ++it)
-        if (tid + it * NT < A_CH) ra[it] = ld16(a_src[it] + off);
+      for (int it = 0; it < A_IT; ++it) ra[it] = ld16(a_src[it] + off);
 #pragma unroll
-      for (int it = 0; it < B_IT; ++it)
-        if (tid + it * NT < B_CH) rb[it] = ld16(b_src[it] + off);
+      for (int it = 0; it < B_IT; ++it) rb[it] = ld16(b_src[it] + off);
     };
     auto lstore = [&](const u32x4_t* ra, const u32x4_t* rb, int buf) {
 #pragma unroll
-      for (int it = 0; it < A_IT; ++it)
-        if (tid + it * NT < A_CH) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_lds[it]]) = ra[it];
+      for (int it = 0; it < A_IT; ++it) {
+        char* dst = (!A_SPARE || tid + it * NT < A_CH) ? &s_a[buf][a_lds[it]] : &s_junk[tid * 16];
+        *reinterpret_cast<u32x4_t*>(dst) = ra[it];
+      }
 #pragma unroll
-      for (int it = 0; it < B_IT; ++it)
-        if (tid + it * NT < B_CH) *reinterpret_cast<u32x4_t*>(&s_b[buf][b_lds[it]]) = rb[it];
+      for (int it = 0; it < B_IT; ++it) {
+        char* dst = (!B_SPARE || tid + it * NT < B_CH) ? &s_b[buf][b_lds[it]] : &s_junk[tid * 16];
+        *reinterpret_cast<u32x4_t*>(dst) = rb[it];
+      }
     };
     auto compute = [&](int buf) {
 #pragma unroll
@@ -230,20 +240,20 @@ grouped_gemm_kernel(GemmArgs g) {
     };
 
     gload(ra0, rb0, 0);
-    if (nK > 1) gload(ra1, rb1, 1);
+    gload(ra1, rb1, 1);
     lstore(ra0, rb0, 0);
     __syncthreads();
     for (int ks = 0; ks < nK; ks += 2) {
       // LDS stage 0 holds step ks; registers set 1 hold step ks+1 (in flight)
-      if (ks + 2 < nK) gload(ra0, rb0, ks + 2);
+      gload(ra0, rb0, ks + 2);
       compute(0);
-      if (ks + 1 < nK) lstore(ra1, rb1, 1);
+      lstore(ra1, rb1, 1);  // past the end: a repeated step, never computed
       __syncthreads();
       if (ks + 1 >= nK) break;
       // LDS stage 1 holds step ks+1; registers set 0 hold step ks+2
-      if (ks + 3 < nK) gload(ra1, rb1, ks + 3);
+      gload(ra1, rb1, ks + 3);
       compute(1);
-      if (ks + 2 < nK) lstore(ra0, rb0, 0);
+      lstore(ra0, rb0, 0);
       __syncthreads();
     }
 

@@ -47,7 +47,7 @@ int launch_topk(const float* partials, int nsplit, const float* col_bias, float*
                 hipStream_t st);
 
 // Router GEMM + top-k in one launch (bf16, at most 128 experts, d_model a
-// multiple of 512).
+// multiple of 1024).
 bool router_topk_fused_ok(int T, int E, int d_model, int dtype);
 int launch_router_topk(const void* x, const void* wr, const float* col_bias, float* logits_out,
                        const float* bias, int T, int E, int d, int k, float scaling,

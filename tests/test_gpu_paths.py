@@ -10,7 +10,8 @@ moe_dispatch sorts in one workgroup for at most 4096 assignments and
 1000 experts, and in a histogram / row-scan / scatter sequence otherwise.
 moe_combine holds up to 8 slots per token in one variant and up to 16 in the
 other.  The 256x256 expert kernel cuts the tiles of a last round that is at
-most half full into f = min(8, CUs / tiles left) row slices.  Each case below sits on one side of such a limit and is checked
+most half full into f = min(8, CUs / tiles left) row slices.  With few rows
+per expert the expert GEMMs run in 16-row tiles.  Each case below sits on one side of such a limit and is checked
 against the oracle like every other layer test: routing under the
 certification rule, dispatch arrays bit-exact, outputs within tolerance."""
 
@@ -65,4 +66,15 @@ def test_router_many_tokens_split_k(T, N, Z, k, d):
 def test_expert_gemm_tail_round_slices(T, N, Z, k):
     w = S.Workload("tail_slices", T=T, d_model=512, n_ffn=N, n_zero=Z, d_ff=256, top_k=k,
                    dtype="bf16", bias_var=0.01, seed=24)
+    full_parity(w)
+
+
+@pytest.mark.parametrize("T,d,N,Z,dff,k,bv", [
+    (1, 256, 8, 4, 256, 3, 0.01),       # a single token
+    (100, 512, 64, 32, 256, 6, 0.5),    # ~6 rows per expert, skewed: some experts > 16 rows
+    (300, 768, 96, 32, 512, 8, 0.01),   # ~19 rows per expert: two m-tiles, the second ragged
+])
+def test_few_rows_per_expert_shapes(T, d, N, Z, dff, k, bv):
+    w = S.Workload("few_rows", T=T, d_model=d, n_ffn=N, n_zero=Z, d_ff=dff, top_k=k,
+                   dtype="bf16", bias_var=bv, seed=25)
     full_parity(w)
