@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph",
                     help="how the timed steps whose time gives `value` are launched: each "
-                         "step captured once as a HIP graph and replayed (default), or the "
-                         "library calls issued one by one; both are run and reported")
+                         "step captured once as a HIP graph and replayed (default; the eager "
+                         "run is reported beside it), or the library calls issued one by one "
+                         "(then no graph is captured, e.g. under a counter profiler)")
     ap.add_argument("--scmoe", type=int, default=0, metavar="D_FF",
                     help="shortcut-connected block: time the MoE layer against a dense "
                          "SwiGLU branch of this width on a second stream (e.g. 12288); "
@@ -350,25 +351,27 @@ def main():
     # controller trajectory: the final output and bias must equal the eager
     # run's bit for bit.
     y_eager, bias_eager = buf.y.clone(), bias.clone()
-    graphs = []
+    g_elapsed, graph_match = None, None
+    graphs = [] if args.launch == "graph" else None
     cap = torch.cuda.Stream()  # default priority
-    for i in range(K):
+    for i in range(K if graphs is not None else 0):
         gr = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gr, stream=cap):
             step(i)
         graphs.append(gr)
-    for rep_i in range(2):
-        reset_controller()
-        g0 = time.perf_counter()
-        for gr in graphs:
-            gr.replay()
-        torch.cuda.synchronize()
-        g_elapsed = time.perf_counter() - g0
-    graph_match = bool(torch.equal(buf.y, y_eager) and torch.equal(bias, bias_eager))
-    if not graph_match:
-        print("bench.py: graph replay differs from the eager run", file=sys.stderr)
-        sys.exit(1)
-    del graphs
+    if graphs is not None:
+        for rep_i in range(2):
+            reset_controller()
+            g0 = time.perf_counter()
+            for gr in graphs:
+                gr.replay()
+            torch.cuda.synchronize()
+            g_elapsed = time.perf_counter() - g0
+        graph_match = bool(torch.equal(buf.y, y_eager) and torch.equal(bias, bias_eager))
+        if not graph_match:
+            print("bench.py: graph replay differs from the eager run", file=sys.stderr)
+            sys.exit(1)
+        del graphs
     eager_elapsed = elapsed
     if args.launch == "graph":
         elapsed = g_elapsed
@@ -448,8 +451,9 @@ def main():
                     "p90": float(np.percentile(step_ms, 90))},
         "stages_ms_mean": {n: float(np.mean(v)) for n, v in st_ms.items()},
         "launch": args.launch,
-        "graph": {"tokens_per_s": w.T * K / g_elapsed, "ms_per_step": g_elapsed / K * 1e3,
-                  "matches_eager": graph_match},
+        "graph": None if g_elapsed is None else {
+            "tokens_per_s": w.T * K / g_elapsed, "ms_per_step": g_elapsed / K * 1e3,
+            "matches_eager": graph_match},
         "eager": {"tokens_per_s": w.T * K / eager_elapsed,
                   "ms_per_step": eager_elapsed / K * 1e3},
         "ffn_assignments_per_step_mean": float(np.mean(A)),
