@@ -27,8 +27,10 @@
 //  * Balanced tile heights: an expert with m rows gets ceil(m / 256) tiles of
 //    equal height (a multiple of 32).  A wave runs the MFMAs of only the
 //    32-row blocks that hold rows: the K loop exists once per count of
-//    active blocks, chosen per tile, so a 160-row tile costs 5/8 of a full
-//    one.
+//    active blocks, chosen per tile, so a 160-row tile does 5/8 of the MFMA
+//    work of a full one (its DMA and barriers cost the same).
+//  * A last round of the persistent grid that is at most half full has its
+//    tiles cut into row slices (at least 32 rows each) over the idle CUs.
 //  * 256 x 256 tiles over 8 waves (2 per SIMD) of 128 x 64: one wave's MFMAs
 //    run while the other waits on LDS or DMA.
 //  * Persistent grid, XCD-contiguous tile order (as in gemm.hip); each
