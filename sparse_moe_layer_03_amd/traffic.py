@@ -12,8 +12,9 @@
         Reads rocprofv3 counter_collection CSVs (one counter per run) and
         writes a text summary: per-dispatch KiB of the kernel, the copy's
         KiB per KiB actually moved (the scale), the kernel's scaled bytes per
-        launch, and a hash of the kernel's sources (a reader of the summary
-        can tell whether the kernel changed since the counters were taken).
+        launch, and a hash of the kernel's sources without comments (a
+        reader of the summary can tell whether the kernel's code changed
+        since the counters were taken).
 """
 
 from __future__ import annotations
@@ -29,12 +30,23 @@ import sys
 COPY_BYTES = 1 << 30
 
 
+def code_text(text: str) -> str:
+    """The code of a C++/HIP source: // comments and blank lines removed, so
+    that editing a comment does not invalidate measured counters."""
+    out = []
+    for line in text.splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line.strip():
+            out.append(line)
+    return "\n".join(out)
+
+
 def source_hash(paths) -> str:
     h = hashlib.sha256()
     for p in sorted(paths):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
