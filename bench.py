@@ -83,12 +83,14 @@ def gate_up_units(w, A, U):
 def gate_up_kernel_name(w):
     """Which gate/up kernel the library launches for this shape (the same
     tests the library makes: at least 32 assignments per expert and at least
-    64 tiles for the tall tiles; bf16 and both K lengths multiples of 128 for
-    the 256x256 direct-to-LDS tiles)."""
+    64 tiles, or at least 64 assignments per FFN expert, for the tall tiles;
+    bf16 and both K lengths multiples of 128 for the 256x256 direct-to-LDS
+    tiles)."""
     E = w.n_ffn + w.n_zero
     Tk = w.T * w.top_k
     cdiv = lambda a, b: -(-a // b)  # noqa: E731
-    tall = Tk // E >= 32 and cdiv(Tk, 128) * cdiv(min(w.d_ff, w.d_model), 128) >= 64
+    tall = ((Tk // E >= 32 and cdiv(Tk, 128) * cdiv(min(w.d_ff, w.d_model), 128) >= 64)
+            or Tk // w.n_ffn >= 64)
     if (tall and w.dtype == "bf16" and w.d_model % 128 == 0 and w.d_ff % 128 == 0
             and cdiv(Tk, 256) * min(w.d_ff // 128, w.d_model // 256) >= 64):
         return "grouped_gemm_big_kernel<1,4> (256x256 tiles, gate/up + SwiGLU)"

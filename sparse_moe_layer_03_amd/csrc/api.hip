@@ -112,16 +112,18 @@ static WsLayout ws_layout(const moe_shape* s) {
 }
 
 // Tile shape of the expert GEMMs.  Rows per expert (T*k/E) of at least 32
-// make tall tiles worth it, but only if there are enough of them to spread
-// over the chip: a dense batch of 128 rows through one expert (T*k/E = 128)
-// gives a single row of tiles, so 16-row tiles are used for it.
+// make tall tiles worth it if there are enough of them to spread over the
+// chip.  With 64 or more rows per FFN expert they are used regardless: 16-row
+// tiles would re-read every weight slice 4 or more times (a dense branch of
+// 128 tokens: 0.37 -> 0.31 ms).
 static constexpr long kMinTiles = 64;
 
 // 128x128 tiles (else 16x128) for the general kernel.
 static int ffn_big_tiles(const moe_shape* s) {
   const long E = (long)s->n_ffn + s->n_zero;
   const long Tk = (long)s->T * s->top_k;
-  return Tk / E >= 32 && cdiv(Tk, 128) * cdiv(std::min(s->d_ff, s->d_model), 128) >= kMinTiles;
+  return (Tk / E >= 32 && cdiv(Tk, 128) * cdiv(std::min(s->d_ff, s->d_model), 128) >= kMinTiles) ||
+         Tk / s->n_ffn >= 64;
 }
 
 // The many-row expert GEMMs (gate/up and down together) need bf16, both K
