@@ -26,6 +26,13 @@ same steps are replayed once with an event at every stage boundary
 touched experts per step for the roofline, load variance per batch), and,
 for the workloads whose data can stay in L2 / Infinity Cache, once more
 with 512 MiB written between steps ("cold", event-timed steps only).
+
+`roofline` is the dominant kernel's (gate/up); `layer` is the whole step's,
+from each step's exact FFN assignments A and touched FFN experts U:
+F = 2 T d E + 6 A d d_ff flops, B_min = the touched experts' weights, the
+router matrix, x, y and the routing outputs; mfma_frac = sum F / (t * peak),
+hbm_frac = sum B_min / (t * 8 TB/s), roofline_frac = sum max(F / peak,
+B_min / 8 TB/s) / t, with t the wall time of the run that gives `value`.
 """
 
 from __future__ import annotations
@@ -430,6 +437,21 @@ def main():
     roof["traffic"] = measured_traffic(w.name)
     roof["kernel"] = "%s, mean %.4f ms/launch" % (gate_up_kernel_name(w), gu_s.mean() * 1e3)
 
+    # whole-layer figures per step from its exact A (FFN assignments) and U
+    # (touched FFN experts): F = 2 T d E + 6 A d d_ff flops; B_min = the
+    # touched experts' weights + router matrix + x and y + idx and gates
+    el = 2 if w.dtype == "bf16" else 4
+    E_ = w.n_ffn + w.n_zero
+    F = 2.0 * w.T * w.d_model * E_ + 6.0 * A * w.d_model * w.d_ff
+    Bmin = (3.0 * el * U * w.d_model * w.d_ff + el * E_ * w.d_model + 2.0 * el * w.T * w.d_model
+            + 8.0 * w.T * w.top_k)
+    tstar = np.maximum(F / peak_fl, Bmin / PEAK_HBM)
+    layer = {"flop_per_step": float(F.mean()), "bytes_min_per_step": float(Bmin.mean()),
+             "mfma_frac": float(F.sum() / (elapsed * peak_fl)),
+             "hbm_frac": float(Bmin.sum() / (elapsed * PEAK_HBM)),
+             "roofline_frac": float(tstar.sum() / elapsed),
+             "bound": "mfma" if (F / peak_fl).sum() >= (Bmin / PEAK_HBM).sum() else "hbm"}
+
     tokens = w.T * K
     value = tokens / elapsed
     line = {
@@ -449,6 +471,7 @@ def main():
                    "n_zero": w.n_zero, "d_ff": w.d_ff, "top_k": w.top_k,
                    "pid": list(w.pid) if w.pid else None},
         "roofline": roof,
+        "layer": layer,
         "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
                     "p90": float(np.percentile(step_ms, 90))},
         "stages_ms_mean": {n: float(np.mean(v)) for n, v in st_ms.items()},
