@@ -123,6 +123,18 @@ def measured_traffic(workload):
     return float(summ["traffic_bytes"])
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, m, budget_s=12.0):
     """Time the oracle (as it stands) on the host cores: whole batches of the
     workload, in order, until about ``budget_s`` seconds of oracle work."""
@@ -501,6 +513,7 @@ def main():
         v, threads, secs, nb = cpu_baseline(w, m)
         line["cpu_baseline"] = {
             "value": v, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"first {nb} whole batch(es) ({nb * w.T} tokens) of the same workload "
                       f"and inputs: oracle route+dispatch+FFN+combine"
                       f"{'+PID' if w.pid else ''} in float64, {secs:.1f} s"}
