@@ -501,6 +501,10 @@ def main():
     if w.pid:
         line["r_per_step"] = [round(float(a) / w.T, 4) for a in A]
         line["ms_per_batch"] = [round(float(v), 4) for v in step_ms]
+        # each batch's whole-layer roofline fraction: max(F/peak, B_min/HBM)
+        # over its event-timed (eager) step time
+        line["layer_roofline_frac_per_batch"] = [
+            round(float(ts / (ms * 1e-3)), 3) for ts, ms in zip(tstar, step_ms)]
         ll = loads[:, : w.n_ffn].astype(np.float64)
         line["ffn_load_max_over_mean_per_step"] = [
             round(float(r.max() / max(r.mean(), 1e-9)), 2) for r in ll]
