@@ -351,6 +351,8 @@ int launch_topk(const float* partials, int nsplit, const float* col_bias, float*
     MOE_TOPK(4);
   else if (E <= 512)
     MOE_TOPK(8);
+  else if (E <= 768)
+    MOE_TOPK(12);
   else
     MOE_TOPK(16);
 #undef MOE_TOPK

@@ -109,6 +109,7 @@ def test_ffn_stage_with_oracle_dispatch_arrays():
 @pytest.mark.parametrize("dtype,d,N,Z,k", [
     ("bf16", 1024, 80, 40, 8),    # router and top-k in one kernel
     ("f32", 128, 200, 100, 12),   # top-k kernel, 5 experts per lane
+    ("f32", 128, 450, 150, 12),   # top-k kernel, 12 experts per lane (the last partly past E)
     ("bf16", 256, 700, 300, 16),  # top-k kernel, 16 experts per lane
 ])
 def test_exact_ties_pick_lowest_ids(dtype, d, N, Z, k):
