@@ -24,6 +24,11 @@
 //    that the stage being read is not one being filled and emits no vmcnt
 //    wait between them.  Each K-step waits (vmcnt) only for its own stages,
 //    then one s_barrier.
+//  * The direct-to-LDS loads of a main-loop step are issued two per MFMA
+//    K-slice (token rows in the first two slices, weights in the last two),
+//    not all after the barrier: their issue stalls until earlier ones have
+//    drained into LDS, and eight waves issuing at once had kept every SIMD's
+//    MFMAs waiting for about a third of each step.
 //  * Balanced tile heights: an expert with m rows gets ceil(m / 256) tiles of
 //    equal height (a multiple of 32).  A wave runs the MFMAs of only the
 //    32-row blocks that hold rows: the K loop exists once per count of
@@ -306,8 +311,17 @@ grouped_gemm_big_kernel(GemmArgs g) {
       for (int q = 0; q < A_PW; ++q) asm volatile("" : "+v"(a_off[q]));
 #pragma unroll
       for (int q = 0; q < B_PW; ++q) asm volatile("" : "+v"(b_off[q]));
-      if (next_a) issue_a(std::integral_constant<int, (AS + 1) % 2>{}, ks + 1);
-      if (next_b) issue_b(std::integral_constant<int, (BS + 2) % 3>{}, ks + 2);
+      // Main-loop steps (both refills compile-time true) spread their DMA
+      // issue over the MFMA slices: a direct-to-LDS load can block issue
+      // until earlier ones drain, and all waves issuing theirs at the step
+      // start would stall their MFMAs together.  Token rows go first (the
+      // step-start vmcnt wait allows only the weights to be in flight).
+      constexpr bool SPREAD = std::is_same_v<decltype(nac), std::true_type> &&
+                              std::is_same_v<decltype(nbc), std::true_type>;
+      if constexpr (!SPREAD) {
+        if (next_a) issue_a(std::integral_constant<int, (AS + 1) % 2>{}, ks + 1);
+        if (next_b) issue_b(std::integral_constant<int, (BS + 2) % 3>{}, ks + 2);
+      }
       // favour this wave's MFMA issue over the other wave on the SIMD
       __builtin_amdgcn_s_setprio(1);
       u32x4_t af[2][MBA], bfr[2][NB];
@@ -324,10 +338,44 @@ grouped_gemm_big_kernel(GemmArgs g) {
           bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * RB + (swz(r, c) << 4)]);
         }
       };
+      // DMA pieces of slice kk: A loads 2kk, 2kk+1 (kk < 2), B loads 2(kk-2), 2(kk-2)+1
+      auto dma_piece = [&](int kk) {
+        if (kk < 2) {
+          char* sa2 = stage_a(std::integral_constant<int, (AS + 1) % 2>{});
+          const size_t off = (size_t)(ks + 1) * RB;
+#pragma unroll
+          for (int q = 2 * kk; q < 2 * kk + 2; ++q)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
+                                             (lds_void_t*)(sa2 + (wave + q * NW) * 1024), 16, 0, 0);
+        } else {
+          char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
+          const size_t off = (size_t)(ks + 2) * RB;
+#pragma unroll
+          for (int q = 2 * (kk - 2); q < 2 * (kk - 2) + 2; ++q) {
+            const char* bb = (MODE == 1 && (q * NW) * RPK >= HN) ? b_base1 : b_base0;
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
+                                             (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, 0);
+          }
+        }
+      };
+      static_assert(!SPREAD || (A_PW == 4 && B_PW == 4 && NKK == 4), "two DMA loads per slice");
+      // Pin the schedule (the default one sinks every LDS read next to its
+      // first use and stalls on it): the first slice's reads, then each
+      // slice's MFMAs with the next slice's reads interleaved 1:1 at the
+      // front, so they have landed before that slice starts.  Main-loop
+      // steps place one DMA load before each half of a slice's pairs; a
+      // scheduling fence after every slice keeps the token-row loads ahead of
+      // the weight loads, which the step-start vmcnt wait relies on.
+      constexpr int NR = MBA + NB;       // LDS reads per slice
+      constexpr int NM = MBA * NB;       // MFMAs per slice
+      constexpr int NP = NR < NM ? NR : NM;
+      constexpr int H1 = NP / 2;
       load(0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         if (kk + 1 < NKK) load((kk + 1) & 1, kk + 1);
+        if constexpr (SPREAD) dma_piece(kk);
 #pragma unroll
         for (int i = 0; i < MBA; ++i)
 #pragma unroll
@@ -335,26 +383,29 @@ grouped_gemm_big_kernel(GemmArgs g) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8_t, bfr[kk & 1][j]),
                 __builtin_bit_cast(bf16x8_t, af[kk & 1][i]), acc[i][j], 0, 0, 0);
-      }
-      // Pin the schedule (the default one sinks every LDS read next to its
-      // first use and stalls on it): the first slice's reads, then each
-      // slice's MFMAs with the next slice's reads interleaved 1:1 at the
-      // front, so they have landed before that slice starts.
-      constexpr int NR = MBA + NB;       // LDS reads per slice
-      constexpr int NM = MBA * NB;       // MFMAs per slice
-      constexpr int NP = NR < NM ? NR : NM;
-      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+        if (kk + 1 < NKK) {
+          if constexpr (SPREAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
 #pragma unroll
-      for (int kk = 0; kk + 1 < NKK; ++kk) {
+          for (int q = 0; q < H1; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+          if constexpr (SPREAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
 #pragma unroll
-        for (int q = 0; q < NP; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          for (int q = H1; q < NP; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+          if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
+          if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+        } else {
+          if constexpr (SPREAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+          if constexpr (SPREAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, NM - NM / 2, 0);
         }
-        if constexpr (NR > NP) __builtin_amdgcn_sched_group_barrier(0x100, NR - NP, 0);
-        if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
+        if constexpr (SPREAD) __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
       __builtin_amdgcn_s_setprio(0);
     };
 
