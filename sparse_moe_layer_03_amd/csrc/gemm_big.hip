@@ -286,10 +286,11 @@ grouped_gemm_big_kernel(GemmArgs g) {
 
     // One K-step of 64 on token-row stage AS and weight stage BS, with MBA
     // active 32-row blocks: wait for this step's stages (the weight stage of
-    // the next step may stay in flight), barrier, refill the stages the
-    // previous step read (token rows one step ahead, weights two), then 4
-    // MFMA K-slices of 16 with the fragments of slice kk+1 read from LDS
-    // while slice kk computes.  nac / nbc: whether the step issues the token
+    // the next step may stay in flight), barrier, then 4 MFMA K-slices of 16
+    // with the fragments of slice kk+1 read from LDS while slice kk computes,
+    // refilling the stages the previous step read (token rows one step
+    // ahead, weights two) — spread over the slices in the main loop, right
+    // after the barrier in the tail.  nac / nbc: whether the step issues the token
     // rows of step ks+1 / the weights of step ks+2.  In the main loop they
     // are compile-time true, so the compiler knows exactly which DMA is still
     // in flight and adds no wait of its own.
