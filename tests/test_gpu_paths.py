@@ -78,3 +78,16 @@ def test_few_rows_per_expert_shapes(T, d, N, Z, dff, k, bv):
     w = S.Workload("few_rows", T=T, d_model=d, n_ffn=N, n_zero=Z, d_ff=dff, top_k=k,
                    dtype="bf16", bias_var=bv, seed=25)
     full_parity(w)
+
+
+@pytest.mark.parametrize("T,N,Z,k,bv", [
+    (2000, 8, 4, 2, 0.01),   # ~500 rows per expert: full 256-row tiles
+    (2000, 8, 4, 2, 0.5),    # skewed: 1-3 tiles per expert, 160-row and short tiles
+])
+def test_expert_gemm_main_loop_and_tail(T, N, Z, k, bv):
+    # 256x256 expert kernel with K-steps in both its unrolled main loop and
+    # its tail: gate/up K = d_model 1024 (16 steps: 12 + 4), down K = d_ff
+    # 640 (10 steps: 6 + 4), 5 and 4 column tiles
+    w = S.Workload("main_and_tail", T=T, d_model=1024, n_ffn=N, n_zero=Z, d_ff=640, top_k=k,
+                   dtype="bf16", bias_var=bv, seed=26)
+    full_parity(w)
