@@ -123,7 +123,8 @@ int moe_device_cu_count(void);
  *   logits_out [T, E] fp32 or NULL (written when given);
  *   ws: workspace (required; holds the K-split partial logits of the
  *       two-kernel path; with at most 128 experts in bf16 the GEMM and the
- *       selection run in one kernel and ws is not touched). */
+ *       selection run in one kernel, and ws holds a copy of w_router
+ *       repacked for it, rewritten on every call). */
 int moe_route(const moe_shape* shape, const void* x, const void* w_router,
               const float* logit_bias, const float* bias, int32_t* topk_idx,
               float* topk_gate, float* logits_out, void* ws, void* stream);

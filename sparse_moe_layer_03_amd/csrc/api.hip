@@ -62,7 +62,7 @@ static bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 struct WsLayout {
-  size_t logits, hist, h, total;
+  size_t logits, hist, h, wrp, total;
 };
 
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -107,6 +107,9 @@ static WsLayout ws_layout(const moe_shape* s) {
   off = up256(off + E * (size_t)dispatch_blocks((long)Tk) * sizeof(int32_t));
   w.h = off;
   off = up256(off + Tk * (size_t)s->d_ff * elem_size(s->dtype));
+  w.wrp = off;  // router matrix repacked for the fused router + top-k kernel
+  if (router_topk_fused_ok(s->T, (int)E, s->d_model, s->dtype))
+    off = up256(off + router_packed_bytes((int)E, s->d_model));
   w.total = off;
   return w;
 }
@@ -190,8 +193,9 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
   hipStream_t st = (hipStream_t)stream;
   const int E = s->n_ffn + s->n_zero;
   if (router_topk_fused_ok(s->T, E, s->d_model, s->dtype))
-    return launch_router_topk(x, w_router, logit_bias, logits_out, bias, s->T, E, s->d_model,
-                              s->top_k, s->routed_scaling, topk_idx, topk_gate, st);
+    return launch_router_topk(x, w_router, (char*)ws + ws_layout(s).wrp, logit_bias, logits_out,
+                              bias, s->T, E, s->d_model, s->top_k, s->routed_scaling, topk_idx,
+                              topk_gate, st);
   const RouterPlan plan = router_plan(s);
   const int nsplit = plan.ksplit;
   float* partials = (float*)((char*)ws + ws_layout(s).logits);

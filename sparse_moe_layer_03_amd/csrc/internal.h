@@ -49,7 +49,10 @@ int launch_topk(const float* partials, int nsplit, const float* col_bias, float*
 // Router GEMM + top-k in one launch (bf16, at most 128 experts, d_model a
 // multiple of 1024).
 bool router_topk_fused_ok(int T, int E, int d_model, int dtype);
-int launch_router_topk(const void* x, const void* wr, const float* col_bias, float* logits_out,
+// Workspace bytes of the router matrix repacked for that kernel.
+size_t router_packed_bytes(int E, int d_model);
+int launch_router_topk(const void* x, const void* wr, void* wr_packed, const float* col_bias,
+                       float* logits_out,
                        const float* bias, int T, int E, int d, int k, float scaling,
                        int32_t* idx, float* gate, hipStream_t st);
 

@@ -194,17 +194,35 @@ topk_kernel(const float* __restrict__ partials, int nsplit, const float* __restr
   select_topk<PL, 1>(l1, m1, s_bias, E, k, scaling, t1, idx, gate);
 }
 
+// The router matrix in the operand order of v_mfma_f32_16x16x32_bf16, so
+// that each load of the fused kernel reads 1 KiB whole (in row order every
+// instruction touched 16 rows x 64 bytes, half a cache line each, and the
+// K loop was bound by the request count): block (K-step ks of 32, column
+// block c) holds, for lane l, expert 16c + (l % 16) (rows past E repeat row
+// E - 1) and K elements 32 ks + 8 (l / 16) .. + 7.  Written into the
+// workspace on every call (the library keeps nothing between calls).
+__global__ void __launch_bounds__(256)
+pack_router_kernel(const __bf16* __restrict__ wr, int E, int d, int ncb,
+                   u32x4_t* __restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // (ks, c, lane)
+  if (i >= (d / 32) * ncb * 64) return;
+  const int lane = i & 63, c = (i >> 6) % ncb, ks = (i >> 6) / ncb;
+  const int e = min(16 * c + (lane & 15), E - 1);
+  out[i] = *reinterpret_cast<const u32x4_t*>(wr + (size_t)e * d + 32 * ks + 8 * (lane >> 4));
+}
+
 // Router GEMM and top-k in one launch, for at most 128 experts in bf16
 // (d_model a multiple of 128 * NW).  A workgroup takes 16 tokens and all
 // experts (in ceil(E / 16) column blocks of 16).  Wave w of NW multiplies them by the router over the K slice w
 // with v_mfma_f32_16x16x32_bf16, operands loaded straight from global memory
-// into registers with P K-steps of 32 in flight; the slices' products are
+// (x by rows, the router matrix packed as above) into registers with P
+// K-steps of 32 in flight; the slices' products are
 // summed in LDS in slice order, and each wave then selects for 16/NW of the
 // tokens at once.  Every workgroup reads the whole router matrix, so the
 // limit is how many loads each CU keeps in flight: hence NW waves.
 template <int NCB, int NW>
 __global__ void __launch_bounds__(64 * NW)
-router_topk_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ wr,
+router_topk_kernel(const __bf16* __restrict__ x, const u32x4_t* __restrict__ wr_packed,
                    const float* __restrict__ col_bias, float* __restrict__ logits_out,
                    const float* __restrict__ bias, int T, int E, int d, int k, float scaling,
                    int32_t* __restrict__ idx, float* __restrict__ gate) {
@@ -231,13 +249,8 @@ router_topk_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ wr,
   // the end are clamped (their products are never used)
   const int xr = min(t0 + r16, T - 1);
   const char* xa = (const char*)x + ((size_t)xr * d + (size_t)w * kq + oct * 8) * 2;
-  uint32_t wo[NCB];
-#pragma unroll
-  for (int c = 0; c < NCB; ++c) {
-    const int e = min(16 * c + r16, E - 1);
-    wo[c] = (uint32_t)(((size_t)e * d + (size_t)w * kq + oct * 8) * 2);
-  }
-  const char* wb = (const char*)wr;
+  // this wave's first packed block (global K-step w * nsteps, column 0)
+  const u32x4_t* wpk = wr_packed + (size_t)w * nsteps * NCB * 64 + lane;
 
   f32x4 acc[NCB];
 #pragma unroll
@@ -247,7 +260,7 @@ router_topk_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ wr,
     fx[slot] = *reinterpret_cast<const u32x4_t*>(xa + st * 64);
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
-      fw[slot][c] = *reinterpret_cast<const u32x4_t*>(wb + wo[c] + st * 64);
+      fw[slot][c] = wpk[((size_t)st * NCB + c) * 64];
   };
 #pragma unroll
   for (int u = 0; u < P; ++u) fetch(u, u);
@@ -306,15 +319,23 @@ bool router_topk_fused_ok(int T, int E, int d_model, int dtype) {
   return dtype == MOE_BF16 && E <= 128 && d_model % (128 * MOE_ROUTER_WAVES) == 0 && T >= 1;
 }
 
-int launch_router_topk(const void* x, const void* wr, const float* col_bias, float* logits_out,
-                       const float* bias, int T, int E, int d, int k, float scaling,
-                       int32_t* idx, float* gate, hipStream_t st) {
+size_t router_packed_bytes(int E, int d_model) {
+  return (size_t)((E + 15) / 16) * 16 * d_model * 2;
+}
+
+int launch_router_topk(const void* x, const void* wr, void* wr_packed, const float* col_bias,
+                       float* logits_out, const float* bias, int T, int E, int d, int k,
+                       float scaling, int32_t* idx, float* gate, hipStream_t st) {
   constexpr int NW = MOE_ROUTER_WAVES;
   const dim3 grid((T + 15) / 16), block(64 * NW);
+  const int ncb = (E + 15) / 16;  // <= 8
+  const int npack = (d / 32) * ncb * 64;
+  hipLaunchKernelGGL(pack_router_kernel, dim3((npack + 255) / 256), dim3(256), 0, st,
+                     (const __bf16*)wr, E, d, ncb, (u32x4_t*)wr_packed);
 #define MOE_RT(NCB)                                                                         \
   hipLaunchKernelGGL((router_topk_kernel<NCB, NW>), grid, block, 0, st, (const __bf16*)x,    \
-                     (const __bf16*)wr, col_bias, logits_out, bias, T, E, d, k, scaling, idx, \
-                     gate)
+                     (const u32x4_t*)wr_packed, col_bias, logits_out, bias, T, E, d, k,      \
+                     scaling, idx, gate)
   switch ((E + 15) / 16) {
     case 1: MOE_RT(1); break;
     case 2: MOE_RT(2); break;
