@@ -63,13 +63,18 @@ combine_kernel(const T* __restrict__ x, const T* __restrict__ y_perm,
   const float gz = s_gz;
   const size_t xrow = (size_t)t * d;
   for (int c = threadIdx.x; c < d / CE; c += 256) {
-    // issue every slot's load before accumulating (in slot order)
+    // issue every slot's load before accumulating (in slot order); y_perm,
+    // x and y are touched once here, so they bypass the caches' retention
+    // (non-temporal: prefill combine 0.40 -> 0.36 ms)
     u32x4_t raw[MAXK];
 #pragma unroll
     for (int f = 0; f < MAXK; ++f)
-      if (f < nf) raw[f] = ld16(y_perm + (size_t)s_row[f] * d + c * CE);
+      if (f < nf)
+        raw[f] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(y_perm + (size_t)s_row[f] * d + c * CE));
     u32x4_t rx = {0, 0, 0, 0};
-    if (gz != 0.f) rx = ld16(x + xrow + c * CE);
+    if (gz != 0.f)
+      rx = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + xrow + c * CE));
     float acc[CE];
 #pragma unroll
     for (int i = 0; i < CE; ++i) acc[i] = 0.f;
@@ -89,7 +94,8 @@ combine_kernel(const T* __restrict__ x, const T* __restrict__ y_perm,
 #pragma unroll
       for (int i = 0; i < CE; ++i) acc[i] += gz * v[i];
     }
-    st16(y + xrow + c * CE, pack16(acc, (T*)nullptr));
+    __builtin_nontemporal_store(pack16(acc, (T*)nullptr),
+                                reinterpret_cast<u32x4_t*>(y + xrow + c * CE));
   }
 }
 

@@ -192,13 +192,21 @@ grouped_gemm_kernel(GemmArgs g) {
     // Every thread loads every step (steps past the end repeat the last one,
     // threads past the tile's chunks repeat a valid chunk): a load under a
     // condition makes the compiler drain all loads in flight at that point.
+    // Expert weights in the few-rows-per-expert tiles are read by one row
+    // tile each and never again in the step: they are loaded non-temporal
+    // (decode gate/up 3.65 -> 3.32 ms, down 1.88 -> 1.80).  The router matrix
+    // is re-read by every row tile and stays cached.
+    constexpr bool B_STREAM = MODE != MODE_ROUTER && BM <= 32;
     u32x4_t ra0[A_IT], rb0[B_IT], ra1[A_IT], rb1[B_IT];
     auto gload = [&](u32x4_t* ra, u32x4_t* rb, int ks) {
       const size_t off = k_off + (size_t)min(ks, nK - 1) * 128;
 #pragma unroll
       for (int it = 0; it < A_IT; ++it) ra[it] = ld16(a_src[it] + off);
 #pragma unroll
-      for (int it = 0; it < B_IT; ++it) rb[it] = ld16(b_src[it] + off);
+      for (int it = 0; it < B_IT; ++it)
+        rb[it] = B_STREAM ? __builtin_nontemporal_load(
+                                reinterpret_cast<const u32x4_t*>(b_src[it] + off))
+                          : ld16(b_src[it] + off);
     };
     auto lstore = [&](const u32x4_t* ra, const u32x4_t* rb, int buf) {
 #pragma unroll
