@@ -113,7 +113,27 @@ grouped_gemm_kernel(GemmArgs g) {
   const int nK = g.K / BK / ksplit;  // K-steps per split (the host divides evenly)
   const size_t a_row_bytes = (size_t)g.K * sizeof(T);
 
-  for (long tt = vid; tt < total; tt += G) {
+  // LDS slots of this thread's chunks (the same in every tile)
+  int a_lds[A_IT], b_lds[B_IT];
+#pragma unroll
+  for (int it = 0; it < A_IT; ++it) {
+    const int q = tid + it * NT, r = q >> 3, c = q & 7;
+    a_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
+  }
+#pragma unroll
+  for (int it = 0; it < B_IT; ++it) {
+    const int q = tid + it * NT, r = q >> 3, c = q & 7;
+    b_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
+  }
+
+  // A tile: its place in the output and this thread's source chunks (at the
+  // start of its K range)
+  struct Tile {
+    int split, row0, rows, m0, n0;
+    const char* a[A_IT];
+    const char* b[B_IT];
+  };
+  auto setup = [&](long tt, Tile& tl) {
     const int split = (int)(tt % ksplit);
     const long t = tt / ksplit;
     const size_t k_off = (size_t)split * nK * 128;  // byte offset of this split's K range
@@ -137,11 +157,11 @@ grouped_gemm_kernel(GemmArgs g) {
     const int rows = (MODE == MODE_ROUTER) ? g.M : (g.offsets[grp + 1] - row0);
     const int m0 = mi * BM;
     const int n0 = nt * HN;
-
-    // ---- per-thread source pointers for this tile
-    const char* a_src[A_IT];
-    const char* b_src[B_IT];
-    int a_lds[A_IT], b_lds[B_IT];
+    tl.split = split;
+    tl.row0 = row0;
+    tl.rows = rows;
+    tl.m0 = m0;
+    tl.n0 = n0;
 #pragma unroll
     for (int it = 0; it < A_IT; ++it) {
       const int q = tid + it * NT;
@@ -158,8 +178,7 @@ grouped_gemm_kernel(GemmArgs g) {
       }
       else
         src_row = row0 + rr;
-      a_src[it] = (const char*)g.a + src_row * a_row_bytes + c * 16;
-      a_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
+      tl.a[it] = (const char*)g.a + src_row * a_row_bytes + k_off + c * 16;
     }
 #pragma unroll
     for (int it = 0; it < B_IT; ++it) {
@@ -177,9 +196,31 @@ grouped_gemm_kernel(GemmArgs g) {
         if (n > g.N - 1) n = g.N - 1;
         base = (const char*)g.b0 + (MODE == MODE_DOWN ? (size_t)grp * g.N * a_row_bytes : 0);
       }
-      b_src[it] = base + (size_t)n * a_row_bytes + c * 16;  // q >= B_CH: loaded, not stored
-      b_lds[it] = r * 128 + ((c ^ (r & 7)) << 4);
+      tl.b[it] = base + (size_t)n * a_row_bytes + k_off + c * 16;  // q >= B_CH: loaded, not stored
     }
+  };
+
+  // The last two K-steps of a tile load the first two of the workgroup's
+  // next tile (nK even), so its loads, its group lookup and its gather
+  // indices are in flight under this tile's MFMAs and epilogue; without a
+  // next tile they repeat the last step.
+  const bool chain = nK % 2 == 0;
+  Tile cur, nxt;
+  bool pre = false;  // cur was set up by the previous tile, which also loaded
+                     // its step 0 into LDS stage 0 and step 1 into register set 1
+
+  // Expert weights in the few-rows-per-expert tiles are read by one row
+  // tile each and never again in the step: they are loaded non-temporal
+  // (decode gate/up 3.65 -> 3.32 ms, down 1.88 -> 1.80).  The router matrix
+  // is re-read by every row tile and stays cached.
+  constexpr bool B_STREAM = MODE != MODE_ROUTER && BM <= 32;
+  u32x4_t ra0[A_IT], rb0[B_IT], ra1[A_IT], rb1[B_IT];
+
+  for (long tt = vid; tt < total; tt += G) {
+    if (!pre) setup(tt, cur);
+    const bool more = chain && tt + G < total;
+    if (more) setup(tt + G, nxt);
+    else nxt = cur;
 
     f32x4_t acc[MB][NB];
 #pragma unroll
@@ -189,24 +230,21 @@ grouped_gemm_kernel(GemmArgs g) {
 
     // Two register sets carry the global loads of the next two K-steps, so a
     // load has two K-steps of MFMA work to arrive before it is written to LDS.
-    // Every thread loads every step (steps past the end repeat the last one,
-    // threads past the tile's chunks repeat a valid chunk): a load under a
-    // condition makes the compiler drain all loads in flight at that point.
-    // Expert weights in the few-rows-per-expert tiles are read by one row
-    // tile each and never again in the step: they are loaded non-temporal
-    // (decode gate/up 3.65 -> 3.32 ms, down 1.88 -> 1.80).  The router matrix
-    // is re-read by every row tile and stays cached.
-    constexpr bool B_STREAM = MODE != MODE_ROUTER && BM <= 32;
-    u32x4_t ra0[A_IT], rb0[B_IT], ra1[A_IT], rb1[B_IT];
+    // Every thread loads every step (steps past the end come from the next
+    // tile or repeat the last one, threads past the tile's chunks repeat a
+    // valid chunk): a load under a condition makes the compiler drain all
+    // loads in flight at that point.
     auto gload = [&](u32x4_t* ra, u32x4_t* rb, int ks) {
-      const size_t off = k_off + (size_t)min(ks, nK - 1) * 128;
+      const bool past = ks >= nK;
+      const size_t off = (size_t)(past ? (more ? ks - nK : nK - 1) : ks) * 128;
 #pragma unroll
-      for (int it = 0; it < A_IT; ++it) ra[it] = ld16(a_src[it] + off);
+      for (int it = 0; it < A_IT; ++it) ra[it] = ld16((past ? nxt.a[it] : cur.a[it]) + off);
 #pragma unroll
-      for (int it = 0; it < B_IT; ++it)
-        rb[it] = B_STREAM ? __builtin_nontemporal_load(
-                                reinterpret_cast<const u32x4_t*>(b_src[it] + off))
-                          : ld16(b_src[it] + off);
+      for (int it = 0; it < B_IT; ++it) {
+        const char* p = (past ? nxt.b[it] : cur.b[it]) + off;
+        rb[it] = B_STREAM ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p))
+                          : ld16(p);
+      }
     };
     auto lstore = [&](const u32x4_t* ra, const u32x4_t* rb, int buf) {
 #pragma unroll
@@ -247,10 +285,12 @@ grouped_gemm_kernel(GemmArgs g) {
       }
     };
 
-    gload(ra0, rb0, 0);
-    gload(ra1, rb1, 1);
-    lstore(ra0, rb0, 0);
-    __syncthreads();
+    if (!pre) {
+      gload(ra0, rb0, 0);
+      gload(ra1, rb1, 1);
+      lstore(ra0, rb0, 0);
+      __syncthreads();
+    }
     for (int ks = 0; ks < nK; ks += 2) {
       // LDS stage 0 holds step ks; registers set 1 hold step ks+1 (in flight)
       gload(ra0, rb0, ks + 2);
@@ -261,11 +301,13 @@ grouped_gemm_kernel(GemmArgs g) {
       // LDS stage 1 holds step ks+1; registers set 0 hold step ks+2
       gload(ra1, rb1, ks + 3);
       compute(1);
-      lstore(ra0, rb0, 0);
+      lstore(ra0, rb0, 0);  // past the end: the next tile's step 0
       __syncthreads();
     }
 
     // ---- epilogue: lane holds C[4*kg + v][r16] of each 16x16 block
+    const int m0 = cur.m0, n0 = cur.n0, rows = cur.rows, row0 = cur.row0, split = cur.split;
+    (void)split;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
 #pragma unroll
@@ -295,6 +337,8 @@ grouped_gemm_kernel(GemmArgs g) {
         }
       }
     }
+    cur = nxt;
+    pre = more;
   }
 }
 
