@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,        /* null required pointer, or a size out of range */
-  MOE_EUNSUPPORTED = -2,  /* valid but outside this build's limits (below) */
+  MOE_EUNSUPPORTED = -2,  /* valid but outside the library's limits (below) */
   MOE_EHIP = -3,          /* a HIP launch or query failed                  */
   MOE_ENONFINITE = -4,    /* non-finite host-side parameter                */
   MOE_EALIGN = -5         /* a pointer is not 16-byte aligned              */
