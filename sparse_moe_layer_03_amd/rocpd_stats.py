@@ -1,16 +1,18 @@
 """Summarise a rocprofv3 results database (rocpd SQLite) per kernel:
 calls, total/average/min/max duration.  Reads only the database file.
 
-    python -m sparse_moe_layer_03_amd.rocpd_stats path/to/results.db [--skip N] [name-substring]
+    python -m sparse_moe_layer_03_amd.rocpd_stats path/to/results.db [--skip N | --calls A:B] [name-substring]
 
 --skip N leaves out the first N calls of every kernel (in start order), e.g.
 the warm-up steps of a bench run, so that the averages cover the timed steps.
+--calls A:B keeps calls A..B-1 of every kernel (0-based, in start order), e.g.
+one pass of a bench run.
 """
 import sqlite3
 import sys
 
 
-def main(path, filt=None, skip=0):
+def main(path, filt=None, skip=0, stop=None):
     cur = sqlite3.connect(path).cursor()
     data = {}
     for name, start, dur, gx, wx, v, ag, lds in cur.execute(
@@ -20,7 +22,7 @@ def main(path, filt=None, skip=0):
         d["durs"].append(dur)
     rows = []
     for name, d in data.items():
-        durs = d["durs"][skip:]
+        durs = d["durs"][skip:stop]
         if not durs:
             continue
         rows.append((name, len(durs), sum(durs), sum(durs) / len(durs), min(durs), max(durs),
@@ -38,9 +40,14 @@ def main(path, filt=None, skip=0):
 
 if __name__ == "__main__":
     args = sys.argv[1:]
-    skip = 0
+    skip, stop = 0, None
     if "--skip" in args:
         i = args.index("--skip")
         skip = int(args[i + 1])
         del args[i:i + 2]
-    main(args[0], args[1] if len(args) > 1 else None, skip)
+    if "--calls" in args:
+        i = args.index("--calls")
+        a, b = args[i + 1].split(":")
+        skip, stop = int(a), int(b)
+        del args[i:i + 2]
+    main(args[0], args[1] if len(args) > 1 else None, skip, stop)
