@@ -7,32 +7,46 @@ moe_dispatch -> moe_ffn_gate_up -> moe_ffn_down -> moe_combine, plus
 moe_pid_update on workloads that run the PID.  Inputs are resident in HBM
 before timing starts.  Prints ONE JSON line.
 
-The default workload is T=4096 tokens, d_model=2048, 64 SwiGLU experts
-(d_ff=1024) + 32 identity experts, top-8, bf16, router bias ~ N(0, 0.1),
-PID set point 6 real experts/token (Kp=0.01, Ki=0.001, Kd=0) updated after
-every batch; the timed steps are batches 0..K-1 of that run, starting from
-the initial bias (warm-up steps run first and are then undone).
+Default (--workload headline): the prefill-shaped batch, T=16384 tokens,
+d_model=6144, 512 SwiGLU experts (d_ff=2048) + 256 identity experts, top-12,
+bf16, router bias 0 -- the line's `value`, `roofline` and `cpu_baseline` --
+and, on the same resident weights (38.7 GB), the decode-shaped batch of
+T=128 tokens, reported in the line's `decode` record with its own step time,
+roofline and CPU baseline.  `metric_fracs` gives the two fractions the
+metric is quoted in: prefill whole-layer MFMA fraction of the bf16 peak and
+decode whole-layer HBM fraction.  --workload NAME runs one workload alone
+(small_bf16 and skewed_bf16 run their PID over K batches: the timed steps are
+batches 0..K-1, starting from the initial bias; warm-up steps are undone).
 
 The steps are timed twice over the same batches and controller trajectory:
-issued one call at a time with three HIP events each (step start, gate/up
-start and end, for the step spread and the gate/up duration of the
-roofline), and as one HIP graph per step, captured once and replayed (no
+issued one call at a time with four HIP events each (step start, gate/up
+start and end, down end: the step spread and the expert GEMM durations for
+the roofline), and as one HIP graph per step, captured once and replayed (no
 events inside).  `value` and `ms_per_step` come from the run named by
 --launch (default: graph); both runs are reported, and the graph run's final
 output and bias must equal the eager run's bit for bit.  After them, outside
-the timed region, the
-same steps are replayed once with an event at every stage boundary
-(stages_ms_mean) and every step's expert loads logged (exact assignments and
-touched experts per step for the roofline, load variance per batch), and,
-for the workloads whose data can stay in L2 / Infinity Cache, once more
-with 512 MiB written between steps ("cold", event-timed steps only).
+the timed region, the same steps are replayed once with an event at every
+stage boundary (stages_ms_mean) and every step's expert loads logged (exact
+assignments and touched experts per step for the roofline, load variance per
+batch), and, for the workloads whose data can stay in L2 / Infinity Cache,
+once more with 512 MiB written between steps ("cold", event-timed steps
+only).
 
-`roofline` is the dominant kernel's (gate/up); `layer` is the whole step's,
-from each step's exact FFN assignments A and touched FFN experts U:
-F = 2 T d E + 6 A d d_ff flops, B_min = the touched experts' weights, the
-router matrix, x, y and the routing outputs; mfma_frac = sum F / (t * peak),
-hbm_frac = sum B_min / (t * 8 TB/s), roofline_frac = sum max(F / peak,
-B_min / 8 TB/s) / t, with t the wall time of the run that gives `value`.
+`roofline` is the dominant kernel's (gate/up; `roofline_down` the down
+GEMM's): algorithmic flops and bytes per launch over the event-measured
+launch time, against whichever bound (bf16 MFMA 2.5 PFLOP/s, HBM 8 TB/s) the
+algorithmic work reaches first.  `layer` is the whole step's, from each
+step's exact FFN assignments A and touched FFN experts U: F = 2 T d E +
+6 A d d_ff flops, B_min = the touched experts' weights, the router matrix, x,
+y and the routing outputs; mfma_frac = sum F / (t * peak), hbm_frac = sum
+B_min / (t * 8 TB/s), roofline_frac = sum max(F / peak, B_min / 8 TB/s) / t,
+with t the wall time of the run that gives `value`.
+
+`cpu_baseline` is the CPU oracle timed on the host cores after the GPU runs.
+Small, skewed and tiny batches run whole; for the 512-expert model the
+oracle routes, dispatches, gathers and combines every token, runs the expert
+FFN of a seeded random subset of the touched experts on their rows, and the
+FFN time is scaled by touched experts / subset size (the label says so).
 """
 
 from __future__ import annotations
@@ -58,9 +72,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="small_bf16",
-                    choices=["small_bf16", "decode_bf16", "prefill_bf16", "skewed_bf16",
-                             "tiny_f32"])
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "small_bf16", "decode_bf16", "prefill_bf16",
+                             "skewed_bf16", "tiny_f32"],
+                    help="headline (default) = prefill_bf16 with decode_bf16 on the same "
+                         "weights in a sub-record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph",
                     help="how the timed steps whose time gives `value` are launched: each "
@@ -164,6 +180,64 @@ def cpu_baseline(w, m, budget_s=12.0):
     return n_tok / t_total, threads, t_total, nb
 
 
+def cpu_baseline_sampled(w, m, x, budget_s=12.0, min_experts=4, seed=0):
+    """Time the oracle (as it stands) on one batch of the 512-expert model.
+
+    Every token is routed, dispatched, gathered and combined by the oracle;
+    the expert FFN runs on a seeded random subset of the touched experts
+    (on all their rows) until about ``budget_s`` seconds of FFN work, and its
+    time is scaled by (touched experts / subset size).  bf16 -> float64
+    conversion of inputs and weights is left out of the timed work.
+    Returns (tokens/s, threads, label)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+    from sparse_moe_layer_03_amd import synth as S
+
+    wr = S.to_numpy64(m["wr"])
+    lb = None if m["lb"] is None else m["lb"].cpu().numpy().astype(np.float64)
+    bias = m["bias0"].cpu().numpy().astype(np.float32)
+    x64 = S.to_numpy64(x)
+    t0 = time.perf_counter()
+    r = O.route(x64, wr, bias, w.top_k, w.routed_scaling, lb)
+    d = O.dispatch(r["topk_idx"], w.E)
+    n_rows = int(d["offsets"][w.n_ffn])
+    xp = O.gather_rows(x64, d["perm"], w.top_k, n_rows)
+    t_front = time.perf_counter() - t0
+    counts = d["counts"][: w.n_ffn]
+    touched = np.nonzero(counts)[0]
+    order = np.random.default_rng(seed).permutation(touched)
+    y_perm = np.zeros((n_rows, w.d_model))
+    t_ffn, done, rows = 0.0, 0, 0
+    wall0 = time.perf_counter()
+    for e in order:
+        lo, hi = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        wg, wu, wd = (S.to_numpy64(m["wg"][e]), S.to_numpy64(m["wu"][e]),
+                      S.to_numpy64(m["wd"][e]))
+        t1 = time.perf_counter()
+        y_perm[lo:hi] = O.swiglu_ffn(xp[lo:hi], wg, wu, wd)
+        t_ffn += time.perf_counter() - t1
+        done += 1
+        rows += hi - lo
+        # stop on FFN time, or on wall time (the untimed weight conversion
+        # dominates when experts hold few rows)
+        if done >= min_experts and (t_ffn >= budget_s
+                                    or time.perf_counter() - wall0 >= 2.5 * budget_s):
+            break
+    t2 = time.perf_counter()
+    O.combine(x64, y_perm, r["topk_idx"], r["topk_gate"], d["inv_perm"], w.n_ffn)
+    t_comb = time.perf_counter() - t2
+    scale = len(touched) / done
+    total = t_front + t_ffn * scale + t_comb
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    label = (f"one batch of {w.T} tokens: oracle route+dispatch+gather {t_front:.2f} s and "
+             f"combine {t_comb:.2f} s over all tokens; expert FFN on {done} of the "
+             f"{len(touched)} touched experts ({rows} of {n_rows} rows, seeded random subset) "
+             f"{t_ffn:.2f} s, scaled x{scale:.1f}; float64")
+    return w.T / total, threads, label
+
+
 def scmoe_main(args):
     """MoE layer and the dense SwiGLU branch of a shortcut-connected block:
     each alone, one after the other on one stream, and concurrently on two
@@ -258,36 +332,54 @@ def scmoe_main(args):
     print(json.dumps(line), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer is measured on a single MI355X).", file=sys.stderr)
-        sys.exit(2)
-    if args.scmoe:
-        return scmoe_main(args)
+def build_model(w, dev):
+    """Resident synthetic weights and router state of a workload."""
+    from sparse_moe_layer_03_amd import synth as S
 
+    alpha = None
+    if w.zipf_s:
+        with open(os.path.join(ROOT, "tests", "golden", "zipf_alpha.json")) as f:
+            alpha = json.load(f)["alpha"]
+    wg, wu, wd = S.make_experts(w, dev)
+    return dict(wr=S.make_router(w, dev), bias0=S.make_bias(w, dev),
+                lb=S.zipf_logit_offset(w, alpha, dev) if w.zipf_s else None,
+                wg=wg, wu=wu, wd=wd)
+
+
+def kernel_roofline(name, fl, by, secs, peak_fl):
+    """Roofline of one kernel from its algorithmic flops and bytes per
+    launch and its measured launch times (seconds)."""
+    import numpy as np
+
+    t_fl = np.sum(fl) / peak_fl
+    t_by = np.sum(by) / PEAK_HBM
+    tot = float(np.sum(secs))
+    if t_fl >= t_by:
+        roof = {"bound": "mfma", "achieved": float(np.sum(fl) / tot / 1e12),
+                "peak": peak_fl / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": float(np.sum(by) / tot / 1e9),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    # both fractions, whichever bound applies
+    roof["mfma_frac"] = float(np.sum(fl) / tot / peak_fl)
+    roof["hbm_frac"] = float(np.sum(by) / tot / PEAK_HBM)
+    roof["kernel"] = "%s, mean %.4f ms/launch" % (name, tot / len(secs) * 1e3)
+    return roof
+
+
+def run_workload(w, args, mdl, dev, cpu=True):
+    """Time K steps of workload ``w`` on resident weights ``mdl``; returns
+    the JSON record."""
     import numpy as np
     import torch
 
     from sparse_moe_layer_03_amd import binding as B
     from sparse_moe_layer_03_amd import synth as S
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = "cuda"
-    w = S.WORKLOADS[args.workload]
-    dt = S.torch_dtype(w.dtype)
-    alpha = None
-    if w.zipf_s:
-        with open(os.path.join(ROOT, "tests", "golden", "zipf_alpha.json")) as f:
-            alpha = json.load(f)["alpha"]
-
-    # ---- resident inputs
-    wr = S.make_router(w, dev)
-    bias0 = S.make_bias(w, dev)
+    wr, bias0, lb = mdl["wr"], mdl["bias0"], mdl["lb"]
+    wg, wu, wd = mdl["wg"], mdl["wu"], mdl["wd"]
     bias = bias0.clone()
-    lb = S.zipf_logit_offset(w, alpha, dev) if w.zipf_s else None
-    wg, wu, wd = S.make_experts(w, dev)
     n_x = min(max(args.steps, 1), w.batches) if w.pid else 1
     xs = [S.make_x(w, b, dev) for b in range(n_x)]
     shape = B.make_shape(w.T, w.d_model, w.n_ffn, w.n_zero, w.d_ff, w.top_k, w.dtype,
@@ -296,11 +388,12 @@ def main():
     params = B.MoePidParams(*w.pid) if w.pid else None
     r_log = torch.zeros(max(args.steps, 1) + args.warmup + 1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    load_log = None
 
     def step(i, ev=None):
-        """One step; ev: None, 7 events (every stage boundary) or 3 events
-        (step start, gate/up start, gate/up end: the timed run keeps its
-        event count low, since each record costs GPU time)."""
+        """One step; ev: None, 7 events (every stage boundary) or 4 events
+        (step start, gate/up start, gate/up end, down end: the timed run
+        keeps its event count low, since each record costs GPU time)."""
         x = xs[i % len(xs)]
         full = ev is not None and len(ev) == 7
         if ev is not None:
@@ -316,8 +409,8 @@ def main():
         if ev is not None:
             ev[3 if full else 2].record(stream)
         B.moe_ffn_down(shape, buf.offsets, wd, buf.y_perm, buf.ws)
-        if full:
-            ev[4].record(stream)
+        if ev is not None:
+            ev[4 if full else 3].record(stream)
         B.moe_combine(shape, x, buf.y_perm, buf.topk_idx, buf.topk_gate, buf.inv_perm, buf.y)
         if full:
             ev[5].record(stream)
@@ -331,19 +424,20 @@ def main():
         if full:
             ev[6].record(stream)
 
-    load_log = None
+    def reset_controller():
+        bias.copy_(bias0)
+        buf.pid_state.zero_()
+        r_log.zero_()
+        torch.cuda.synchronize()
 
     # ---- warm-up, then restore the initial controller state
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    bias.copy_(bias0)
-    buf.pid_state.zero_()
-    r_log.zero_()
-    torch.cuda.synchronize()
+    reset_controller()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     ev_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -351,20 +445,14 @@ def main():
         step(i, evs[i])
     ev_end.record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    elapsed = time.perf_counter() - t0
 
     # ---- timed-run durations (HIP events on the launch stream): each step
-    # (start to next start) and each gate/up launch
+    # (start to next start), each gate/up and each down launch
     starts = [evs[i][0] for i in range(K)] + [ev_end]
     step_ms = np.array([starts[i].elapsed_time(starts[i + 1]) for i in range(K)])
     gu_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in range(K)])
-
-    def reset_controller():
-        bias.copy_(bias0)
-        buf.pid_state.zero_()
-        r_log.zero_()
-        torch.cuda.synchronize()
+    dn_ms = np.array([evs[i][2].elapsed_time(evs[i][3]) for i in range(K)])
 
     # ---- the same K steps as HIP graphs: each step (its batch differs) is
     # captured once, the controller is reset, all graphs are replayed once
@@ -381,7 +469,7 @@ def main():
             step(i)
         graphs.append(gr)
     if graphs is not None:
-        for rep_i in range(2):
+        for _ in range(2):
             reset_controller()
             g0 = time.perf_counter()
             for gr in graphs:
@@ -434,25 +522,22 @@ def main():
                     [cevs[i][2].elapsed_time(cevs[i][3]) for i in range(K)]))}
     reset_controller()
 
-    fl, by = zip(*[gate_up_units(w, int(a), int(u)) for a, u in zip(A, U)])
-    gu_s = gu_ms / 1e3
+    el = 2 if w.dtype == "bf16" else 4
     peak_fl = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32_MFMA
-    t_fl = np.sum(fl) / peak_fl
-    t_by = np.sum(by) / PEAK_HBM
-    if t_fl >= t_by:
-        roof = {"bound": "mfma", "achieved": float(np.sum(fl) / gu_s.sum() / 1e12),
-                "peak": peak_fl / 1e12, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": float(np.sum(by) / gu_s.sum() / 1e9),
-                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    fl, by = zip(*[gate_up_units(w, int(a), int(u)) for a, u in zip(A, U)])
+    roof = kernel_roofline(gate_up_kernel_name(w), fl, by, gu_ms / 1e3, peak_fl)
     roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "%s, mean %.4f ms/launch" % (gate_up_kernel_name(w), gu_s.mean() * 1e3)
+    # down: 2 A d d_ff flops; the U experts' down weights, H rows in, y_perm rows out
+    fl_d = [2.0 * a * w.d_model * w.d_ff for a in A]
+    by_d = [el * (1.0 * u * w.d_model * w.d_ff + a * w.d_ff + a * w.d_model)
+            for a, u in zip(A, U)]
+    roof_d = kernel_roofline(gate_up_kernel_name(w).replace("<1,", "<2,")
+                             .replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2"),
+                             fl_d, by_d, dn_ms / 1e3, peak_fl)
 
     # whole-layer figures per step from its exact A (FFN assignments) and U
     # (touched FFN experts): F = 2 T d E + 6 A d d_ff flops; B_min = the
     # touched experts' weights + router matrix + x and y + idx and gates
-    el = 2 if w.dtype == "bf16" else 4
     E_ = w.n_ffn + w.n_zero
     F = 2.0 * w.T * w.d_model * E_ + 6.0 * A * w.d_model * w.d_ff
     Bmin = (3.0 * el * U * w.d_model * w.d_ff + el * E_ * w.d_model + 2.0 * el * w.T * w.d_model
@@ -464,8 +549,7 @@ def main():
              "roofline_frac": float(tstar.sum() / elapsed),
              "bound": "mfma" if (F / peak_fl).sum() >= (Bmin / PEAK_HBM).sum() else "hbm"}
 
-    tokens = w.T * K
-    value = tokens / elapsed
+    value = w.T * K / elapsed
     line = {
         "metric": METRIC,
         "value": value,
@@ -483,6 +567,7 @@ def main():
                    "n_zero": w.n_zero, "d_ff": w.d_ff, "top_k": w.top_k,
                    "pid": list(w.pid) if w.pid else None},
         "roofline": roof,
+        "roofline_down": roof_d,
         "layer": layer,
         "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
                     "p90": float(np.percentile(step_ms, 90))},
@@ -512,18 +597,72 @@ def main():
     if args.balance > 0:
         line["balance_gamma"] = args.balance
 
-    if not args.no_cpu_baseline and w.name in ("small_bf16", "skewed_bf16", "tiny_f32"):
-        m = dict(wr=wr, lb=lb, bias0=bias0, wg=wg, wu=wu, wd=wd, xs=xs)
-        v, threads, secs, nb = cpu_baseline(w, m)
-        line["cpu_baseline"] = {
-            "value": v, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu": cpu_model(), "host_cpus": os.cpu_count(),
-            "sample": f"first {nb} whole batch(es) ({nb * w.T} tokens) of the same workload "
+    line["cpu_baseline"] = None
+    if cpu and not args.no_cpu_baseline:
+        if w.name in ("small_bf16", "skewed_bf16", "tiny_f32"):
+            m = dict(mdl, xs=xs)
+            v, threads, secs, nb = cpu_baseline(w, m)
+            sample = (f"first {nb} whole batch(es) ({nb * w.T} tokens) of the same workload "
                       f"and inputs: oracle route+dispatch+FFN+combine"
-                      f"{'+PID' if w.pid else ''} in float64, {secs:.1f} s"}
-    else:
-        # the decode/prefill model (38.7 GB bf16) does not fit a float64 host copy
-        line["cpu_baseline"] = None
+                      f"{'+PID' if w.pid else ''} in float64, {secs:.1f} s")
+        else:
+            v, threads, sample = cpu_baseline_sampled(w, mdl, xs[0])
+        line["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
+                                "kind": "oracle", "cpu": cpu_model(),
+                                "host_cpus": os.cpu_count(), "sample": sample}
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    if args.scmoe:
+        if args.workload == "headline":
+            args.workload = "decode_bf16"
+        return scmoe_main(args)
+
+    import torch
+
+    from sparse_moe_layer_03_amd import synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    if args.workload != "headline":
+        w = S.WORKLOADS[args.workload]
+        line = run_workload(w, args, build_model(w, dev), dev)
+        print(json.dumps(line), flush=True)
+        return
+
+    # prefill line and decode record on the same resident 512-expert weights
+    wp, wdec = S.WORKLOADS["prefill_bf16"], S.WORKLOADS["decode_bf16"]
+    assert (wp.d_model, wp.n_ffn, wp.n_zero, wp.d_ff, wp.seed) == \
+        (wdec.d_model, wdec.n_ffn, wdec.n_zero, wdec.d_ff, wdec.seed)
+    mdl = build_model(wp, dev)
+    print(f"bench.py: weights resident ({3 * wp.n_ffn * wp.d_model * wp.d_ff * 2 / 1e9:.1f} GB); "
+          "timing prefill_bf16", file=sys.stderr, flush=True)
+    line = run_workload(wp, args, mdl, dev, cpu=False)
+    print("bench.py: timing decode_bf16", file=sys.stderr, flush=True)
+    dec = run_workload(wdec, args, mdl, dev, cpu=False)
+    if not args.no_cpu_baseline:
+        from sparse_moe_layer_03_amd import synth as S2
+        for rec, w in ((line, wp), (dec, wdec)):
+            print(f"bench.py: CPU oracle baseline, {w.name}", file=sys.stderr, flush=True)
+            x = S2.make_x(w, 0, dev)
+            v, threads, sample = cpu_baseline_sampled(w, mdl, x)
+            rec["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": threads,
+                                   "kind": "oracle", "cpu": cpu_model(),
+                                   "host_cpus": os.cpu_count(), "sample": sample}
+    keep = ("value", "unit", "ms_per_step", "config", "roofline", "roofline_down", "layer",
+            "step_ms", "stages_ms_mean", "graph", "eager", "ffn_assignments_per_step_mean",
+            "touched_ffn_experts_per_step_mean", "cpu_baseline")
+    line["decode"] = {k: dec[k] for k in keep}
+    line["metric_fracs"] = {
+        "prefill_mfma_frac": line["layer"]["mfma_frac"],
+        "decode_hbm_frac": dec["layer"]["hbm_frac"],
+        "targets": {"prefill_mfma_frac": 0.60, "decode_hbm_frac": 0.70}}
     print(json.dumps(line), flush=True)
 
 

@@ -37,14 +37,20 @@ Readings where the pages are silent (each is listed in the design notes):
 * Expert ids 0..N-1 are FFN experts, N..E-1 are identity experts.
 * Top-k ties go to the lower expert id; a token's selected set is reported in
   ascending expert id.
-* The selection decision is taken in float32, the precision of the kernel that
-  takes it: key = fp32(fp32(p) + bias) with bias a float32 vector.
+* The selection decision is taken in float32: key = fp32(fp32(p) + bias),
+  with bias a float32 vector.  This is part of the problem statement adopted
+  for this layer (routing scores, correction bias and gates are float32
+  quantities in the C interface), not a property of any implementation.
 * A zero-computation expert returns its input unchanged; the routed scaling
   factor multiplies every gate, identity experts included.
 * SwiGLU expert: H = silu(X Wg^T) * (X Wu^T), Y = H Wd^T, silu(z) = z/(1+e^-z).
 * Dispatch order inside an expert is stable by assignment id a = t*k + j.
 * PID: incremental form on the FFN experts' bias, error measured in real
   (FFN) experts per token, D = 0 on the first update, no anti-windup clamp.
+  The controller is defined in float32 (its state and the bias are float32
+  quantities), each multiply and add rounded on its own in the order
+  delta = (kp*err + ki*I) + kd*D; ``pid_update_f32`` evaluates exactly that,
+  ``pid_update`` the same law in float64 as a cross-check.
 * Per-expert load balancing ([AS] section "MoE专家动态负载均衡": dynamic load
   balancing narrows the gap between experts' token loads; method not
   stated): a zero-sum sign step on the FFN experts' correction bias, so it
@@ -70,6 +76,7 @@ __all__ = [
     "combine",
     "PidState",
     "pid_update",
+    "pid_update_f32",
     "balance_update",
     "forward",
 ]
@@ -107,9 +114,10 @@ def selection_keys(p, bias):
     """Selection key = score + correction bias, in float32.
 
     [DS] "Mixture of experts" names an e_score_correction_bias on the router;
-    it corrects the score used to *choose* experts.  The decision is taken in
-    float32, so the score is rounded to float32 first and the sum is rounded
-    once more.
+    it corrects the score used to *choose* experts.  The layer's problem
+    statement makes scores and the bias float32 quantities, so the decision
+    is taken in float32: the score is rounded to float32 first and the sum
+    is rounded once more.
     """
     p32 = np.asarray(p, dtype=np.float64).astype(np.float32)
     b32 = np.asarray(bias, dtype=np.float32)
@@ -285,6 +293,39 @@ def pid_update(counts, n_ffn, T, bias, state, setpoint, kp, ki, kd):
     new_bias = _f64(bias).copy()
     new_bias[:n_ffn] += delta
     st.prev_err = err
+    st.step += 1
+    return new_bias, st, r
+
+
+def pid_update_f32(counts, n_ffn, T, bias, state, setpoint, kp, ki, kd):
+    """The PID step of ``pid_update`` evaluated in float32, one rounding per
+    operation, in this order:
+
+        r     = f32(sum_{e<N} counts[e]) / f32(T)
+        err   = setpoint - r
+        I     = I + err
+        D     = err - prev_err            (0 on the first update)
+        delta = (kp*err + ki*I) + kd*D    (three products, then two sums)
+        bias[e] = bias[e] + delta         for e < N
+
+    [SN] fixes only that a PID controller moves the router bias; the float32
+    evaluation order is the controller's definition in this layer (its state,
+    gains and the bias are float32 quantities), so two implementations of it
+    can agree bit for bit.  ``state`` holds float32 values; ``bias`` is
+    returned as float32.  Returns (new_bias, new_state, r).
+    """
+    f = np.float32
+    counts = np.asarray(counts, dtype=np.int64)
+    r = f(counts[:n_ffn].sum()) / f(T)
+    err = f(setpoint) - r
+    st = state.copy()
+    integral = f(st.integral) + err
+    d_term = f(0.0) if st.step == 0 else err - f(st.prev_err)
+    delta = (f(kp) * err + f(ki) * integral) + f(kd) * d_term
+    new_bias = np.asarray(bias, dtype=np.float32).copy()
+    new_bias[:n_ffn] = new_bias[:n_ffn] + delta
+    st.integral = f(integral)
+    st.prev_err = f(err)
     st.step += 1
     return new_bias, st, r
 

@@ -5,16 +5,19 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <atomic>
+#include <mutex>
 
 #include <algorithm>
 
 #include "common.h"
 #include "internal.h"
+#include "plan.h"
 
 namespace moe {
 
 static thread_local hipError_t g_last_hip = hipSuccess;
+
+void set_hip_error(hipError_t e) { g_last_hip = e; }
 
 int check_launch() {
   const hipError_t e = hipGetLastError();
@@ -25,21 +28,38 @@ int check_launch() {
   return MOE_OK;
 }
 
+// Multiprocessor count per device, queried once per device (std::call_once;
+// a failed query is remembered as MOE_EHIP).
+constexpr int kMaxDevices = 64;
 int device_cu_count() {
-  static std::atomic<int> cache[64];
-  static std::atomic<bool> init{false};
-  if (!init.load()) {
-    for (auto& c : cache) c.store(-1);
-    init.store(true);
-  }
+  static std::once_flag once[kMaxDevices];
+  static int cache[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EHIP;
-  int n = cache[dev].load();
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    return MOE_EHIP;
-  cache[dev].store(n);
-  return n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::call_once(once[dev], [dev] {
+    int n = 0;
+    const bool ok = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) ==
+                        hipSuccess && n >= 1;
+    cache[dev] = ok ? n : MOE_EHIP;
+  });
+  return cache[dev];
+}
+
+// CUs a stream may use: the set bits of its CU mask (a stream created with
+// hipExtStreamCreateWithCUMask), else the device's CU count.  Persistent
+// grids are sized by it, so a kernel on a partitioned stream does not queue
+// workgroups behind its own.
+int stream_cu_count(hipStream_t st) {
+  const int dev_cus = device_cu_count();
+  if (dev_cus <= 0 || st == nullptr) return dev_cus;
+  uint32_t mask[32] = {};  // up to 1024 CUs
+  if (hipExtStreamGetCUMask(st, 32, mask) != hipSuccess) {
+    (void)hipGetLastError();  // not a launch failure: fall back to the device
+    return dev_cus;
+  }
+  int n = 0;
+  for (uint32_t m : mask) n += __builtin_popcount(m);
+  return (n >= 1 && n < dev_cus) ? n : dev_cus;
 }
 
 static int elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
@@ -66,7 +86,7 @@ struct WsLayout {
 };
 
 static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
-static long cdiv(long a, long b) { return (a + b - 1) / b; }
+using plan::cdiv;
 
 // Router GEMM plan.  The one-kernel router + top-k takes up to 128 experts.
 // Above that, many tokens go through the 256x256 kernel with its K loop
@@ -82,13 +102,15 @@ static RouterPlan router_plan(const moe_shape* s) {
   const int E = s->n_ffn + s->n_zero;
   const RouterPlan general{false, router_ksplit(s->T, E, s->d_model, s->dtype)};
   if (router_topk_fused_ok(s->T, E, s->d_model, s->dtype)) return general;
+  // token rows are addressed from a 64-bit tile base, router rows by 32-bit
+  // offsets ((E * d_model * 2 < 2^32 for E <= 1024 and any int d_model
+  // the workspace can hold))
   if (s->dtype != MOE_BF16 || s->d_model % 128 != 0 || s->T < 512 ||
-      (size_t)s->T * s->d_model * 2 >= (1ull << 32) ||
       (size_t)E * s->d_model * 2 >= (1ull << 32))
     return general;
   const long items = cdiv(s->T, kBigTileRows) * cdiv(E, 256);
   const int nK = s->d_model / 64;
-  const int G = big_grid();
+  const int G = big_grid(nullptr);  // the device's: it sizes the workspace
   int ks = 1;
   while (ks < 8 && items * ks * 2 <= G && nK % (4 * ks) == 0) ks *= 2;
   if (items * ks * 2 < G) return general;  // too few tiles even when split
@@ -114,39 +136,16 @@ static WsLayout ws_layout(const moe_shape* s) {
   return w;
 }
 
-// Tile shape of the expert GEMMs.  Rows per expert (T*k/E) of at least 32
-// make tall tiles worth it if there are enough of them to spread over the
-// chip.  With 64 or more rows per FFN expert they are used regardless: 16-row
-// tiles would re-read every weight slice 4 or more times (a dense branch of
-// 128 tokens: 0.37 -> 0.31 ms).
-static constexpr long kMinTiles = 64;
-
 // 128x128 tiles (else 16x128) for the general kernel.
 static int ffn_big_tiles(const moe_shape* s) {
-  const long E = (long)s->n_ffn + s->n_zero;
-  const long Tk = (long)s->T * s->top_k;
-  return (Tk / E >= 32 && cdiv(Tk, 128) * cdiv(std::min(s->d_ff, s->d_model), 128) >= kMinTiles) ||
-         Tk / s->n_ffn >= 64;
+  return plan::ffn_tall_tiles(s->T, s->top_k, s->n_ffn, s->n_zero, s->d_model, s->d_ff);
 }
 
-// The many-row expert GEMMs (gate/up and down together) need bf16, both K
-// lengths a multiple of 128 (K-steps of 64 in pairs), every operand byte
-// offset within 32 bits (token rows may come from x_perm, which has T*k
-// rows), and enough 256x256 tiles.
-static bool ffn_use_big(const moe_shape* s) {
-  const size_t Tk = (size_t)s->T * s->top_k;
-  if (!(ffn_big_tiles(s) && s->dtype == MOE_BF16 && s->d_model % 128 == 0 &&
-        s->d_ff % 128 == 0 && Tk * s->d_model * 2 < (1ull << 32) &&
-        Tk * s->d_ff * 2 < (1ull << 32) && (size_t)s->d_ff * s->d_model * 2 < (1ull << 32)))
-    return false;
-  const long nt_min = std::min((long)s->d_ff / 128, (long)s->d_model / 256);
-  if (cdiv((long)Tk, 256) * nt_min < kMinTiles) return false;
-  // each workgroup tracks at most 128 tiles (gate/up: d_ff/128 column
-  // tiles per m-tile, down: d_model/256); the m-tile count of the first
-  // group is packed into 22 bits
-  const long mt = big_tile_list_max((long)Tk, s->n_ffn);
-  const long nt = std::max((long)s->d_ff / 128, (long)s->d_model / 256);
-  return mt < (1l << 22) && mt * nt <= 128l * big_grid();
+// The many-row expert GEMMs (256x256 direct-to-LDS tiles); `gather`: gate/up
+// reads x through perm.
+static bool ffn_use_big(const moe_shape* s, bool gather, hipStream_t st) {
+  return plan::ffn_use_big(s->T, s->top_k, s->n_ffn, s->n_zero, s->d_model, s->d_ff,
+                           s->dtype == MOE_BF16, gather, big_grid(st));
 }
 
 // 128x128 router tiles when there are enough of them (prefill), else 16-row
@@ -154,6 +153,32 @@ static bool ffn_use_big(const moe_shape* s) {
 static int router_big_tiles(const moe_shape* s) {
   const int E = s->n_ffn + s->n_zero;
   return router_ksplit(s->T, E, s->d_model, s->dtype) == 1 && (long)(s->T / 128) * ((E + 127) / 128) >= 256;
+}
+
+int dispatch_checks(const moe_shape* s, const int32_t* topk_idx, const void* x,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                    void* x_perm) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!topk_idx || !counts || !offsets || !perm || !inv_perm || (x_perm && !x))
+    return MOE_EINVAL;
+  if (!al4(topk_idx) || !al4(counts) || !al4(offsets) || !al4(perm) || !al4(inv_perm) ||
+      (x_perm && (!al16(x) || !al16(x_perm))))
+    return MOE_EALIGN;
+  return MOE_OK;
+}
+
+int dispatch_run(const moe_shape* s, const int32_t* topk_idx, const void* x,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm,
+                 void* x_perm, int32_t* hist, hipStream_t st) {
+  const int E = s->n_ffn + s->n_zero;
+  const int Tk = s->T * s->top_k;
+  int rc = launch_dispatch(topk_idx, Tk, E, dispatch_blocks(Tk), hist, counts, offsets, perm,
+                           inv_perm, st);
+  if (rc) return rc;
+  if (x_perm)
+    rc = launch_gather(s->dtype, x, perm, offsets, s->n_ffn, Tk, s->top_k, s->d_model, x_perm, st);
+  return rc;
 }
 
 }  // namespace moe
@@ -196,8 +221,8 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
     return launch_router_topk(x, w_router, (char*)ws + ws_layout(s).wrp, logit_bias, logits_out,
                               bias, s->T, E, s->d_model, s->top_k, s->routed_scaling, topk_idx,
                               topk_gate, st);
-  const RouterPlan plan = router_plan(s);
-  const int nsplit = plan.ksplit;
+  const RouterPlan rp = router_plan(s);
+  const int nsplit = rp.ksplit;
   float* partials = (float*)((char*)ws + ws_layout(s).logits);
   GemmArgs g{};
   g.a = x;
@@ -209,7 +234,7 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
   g.ngroups = 1;
   g.top_k = s->top_k;
   g.ksplit = nsplit;
-  rc = plan.big ? launch_gemm_big(0, g, st) : launch_gemm(s->dtype, 0, router_big_tiles(s), g, st);
+  rc = rp.big ? launch_gemm_big(0, g, st) : launch_gemm(s->dtype, 0, router_big_tiles(s), g, st);
   if (rc) return rc;
   return launch_topk(partials, nsplit, logit_bias, logits_out, bias, s->T, E, s->top_k,
                      s->routed_scaling, topk_idx, topk_gate, st);
@@ -218,23 +243,13 @@ int moe_route(const moe_shape* s, const void* x, const void* w_router, const flo
 int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm, void* ws,
                  void* stream) {
-  int rc = check_shape(s);
+  int rc = dispatch_checks(s, topk_idx, x, counts, offsets, perm, inv_perm, x_perm);
   if (rc) return rc;
-  if (!topk_idx || !counts || !offsets || !perm || !inv_perm || !ws || (x_perm && !x))
-    return MOE_EINVAL;
-  if (!al4(topk_idx) || !al4(counts) || !al4(offsets) || !al4(perm) || !al4(inv_perm) ||
-      !al16(ws) || (x_perm && (!al16(x) || !al16(x_perm))))
-    return MOE_EALIGN;
-  hipStream_t st = (hipStream_t)stream;
-  const int E = s->n_ffn + s->n_zero;
-  const int Tk = s->T * s->top_k;
-  const int nb = dispatch_blocks(Tk);
+  if (!ws) return MOE_EINVAL;
+  if (!al16(ws)) return MOE_EALIGN;
   int32_t* hist = (int32_t*)((char*)ws + ws_layout(s).hist);
-  rc = launch_dispatch(topk_idx, Tk, E, nb, hist, counts, offsets, perm, inv_perm, st);
-  if (rc) return rc;
-  if (x_perm)
-    rc = launch_gather(s->dtype, x, perm, offsets, s->n_ffn, Tk, s->top_k, s->d_model, x_perm, st);
-  return rc;
+  return dispatch_run(s, topk_idx, x, counts, offsets, perm, inv_perm, x_perm, hist,
+                      (hipStream_t)stream);
 }
 
 int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const int32_t* perm,
@@ -259,7 +274,8 @@ int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
   g.ksplit = 1;
-  if (ffn_use_big(s)) return launch_gemm_big(1, g, (hipStream_t)stream);
+  if (ffn_use_big(s, x_perm == nullptr, (hipStream_t)stream))
+    return launch_gemm_big(1, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 
@@ -280,7 +296,7 @@ int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down,
   g.top_k = s->top_k;
   g.M = s->T;
   g.ksplit = 1;
-  if (ffn_use_big(s)) return launch_gemm_big(2, g, (hipStream_t)stream);
+  if (ffn_use_big(s, false, (hipStream_t)stream)) return launch_gemm_big(2, g, (hipStream_t)stream);
   return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 

@@ -348,13 +348,14 @@ template <typename T, int MODE, int BM, int BN, int WM, int WN>
 static int launch_cfg(const GemmArgs& g, hipStream_t st) {
   auto kern = grouped_gemm_kernel<T, MODE, BM, BN, WM, WN>;
   constexpr int NT = 64 * WM * WN;
-  static int per_cu = -1;  // occupancy of this instantiation (device-independent here)
-  if (per_cu < 0) {
+  // occupancy of this instantiation, queried once (thread-safe static
+  // initialisation; every device this library runs on is a gfx950)
+  static const int per_cu = [kern] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, 0) != hipSuccess || n < 1) n = 1;
-    per_cu = n;
-  }
-  const int cus = device_cu_count();
+    return n;
+  }();
+  const int cus = stream_cu_count(st);
   if (cus <= 0) return MOE_EHIP;
   int grid = cus * per_cu;
   grid -= grid % 8;

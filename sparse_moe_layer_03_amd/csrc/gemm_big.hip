@@ -45,6 +45,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -68,6 +69,10 @@ __device__ __forceinline__ void wait_lgkm0() {
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
 constexpr int kBigMaxGroups = 1024;
+constexpr int kBigDescRegs = 4;  // tile descriptors: 64 per register
+static_assert(64 * kBigDescRegs == plan::kBigMaxTilesPerWg, "host bound on items per workgroup");
+static_assert(kBigMaxGroups == plan::kBigMaxGroups && kBigTileRows == plan::kBigTileRows,
+              "host plan matches the kernel");
 
 template <int MODE, int MG>
 __global__ void __launch_bounds__(512, 1)
@@ -105,10 +110,10 @@ grouped_gemm_big_kernel(GemmArgs g) {
 
   // ---- this workgroup's tiles.  The per-group m-tile prefix is built in the
   // first token-row stage (no DMA has started yet); lane l of every wave then
-  // looks up the group of tiles vid + l*G and vid + (64 + l)*G and keeps it,
-  // packed with the group's first m-tile, in one register each (the host
-  // guarantees at most 128 tiles per workgroup); the tile loop reads them
-  // back with readlane.
+  // looks up the group of tiles vid + (64 j + l)*G, j < kBigDescRegs, and
+  // keeps it, packed with the group's first m-tile, in register j (the host
+  // guarantees at most 64 * kBigDescRegs tiles per workgroup); the tile loop
+  // reads them back with readlane.
   int* s_pref = reinterpret_cast<int*>(s_a0);  // ngroups + 1 <= 1025 ints
   int* s_scan = reinterpret_cast<int*>(s_a1);  // NT / 64 ints
   {
@@ -157,8 +162,10 @@ grouped_gemm_big_kernel(GemmArgs g) {
     }
     return ((uint32_t)s_pref[lo] << 10) | (uint32_t)lo;
   };
-  const uint32_t tdesc0 = (MODE == 0) ? 0u : find(tile_of(vid + lane * G));
-  const uint32_t tdesc1 = (MODE == 0) ? 0u : find(tile_of(vid + (64 + lane) * G));
+  uint32_t tdesc[kBigDescRegs];
+#pragma unroll
+  for (int j = 0; j < kBigDescRegs; ++j)
+    tdesc[j] = (MODE == 0) ? 0u : find(tile_of(vid + (64 * j + lane) * G));
   __syncthreads();  // the prefix is dead before the first DMA into s_a0
   const int nK = g.K / KS / ksplit;  // per split; the host guarantees an even count
   const size_t row_bytes = (size_t)g.K * 2;
@@ -170,11 +177,17 @@ grouped_gemm_big_kernel(GemmArgs g) {
   const int dma_slot = lane % 8;
 
   for (int k = 0; vid + k * G < total; ++k) {
+    // the host bounds the items per workgroup by 64 * kBigDescRegs (the
+    // descriptor registers); never read past them
+    if (MODE != 0 && k >= 64 * kBigDescRegs) break;
     const int tsplit = (MODE == 0) ? (vid + k * G) / tiles : 0;
     const int it = vid + k * G - tsplit * tiles;  // item (== tile unless sliced)
     const int t = tile_of(it);
-    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane(
-        (int)(k < 64 ? tdesc0 : tdesc1), k & 63);
+    uint32_t dreg = tdesc[0];
+#pragma unroll
+    for (int j = 1; j < kBigDescRegs; ++j)
+      if ((k >> 6) == j) dreg = tdesc[j];
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)dreg, k & 63);
     const int grp = (MODE == 0) ? 0 : (int)(d & 1023u);
     const int tp0 = (MODE == 0) ? 0 : (int)(d >> 10);
     const int cnt_g = (MODE == 0) ? g.M : g.offsets[grp + 1] - g.offsets[grp];
@@ -184,7 +197,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     // major inside a group), so the tiles that run together on one XCD share
     // both their token-row slices and their weight slices in L2.
     const int grp_m0 = (local / (MG * ntiles)) * MG;
-    const int mg = min(MG, mt_g - grp_m0);
+    const int mg = max(1, min(MG, mt_g - grp_m0));
     const int in_grp = local - grp_m0 * ntiles;
     const int nt = in_grp / mg, mi = grp_m0 + in_grp % mg;
     const int row0 = (MODE == 0) ? 0 : g.offsets[grp];
@@ -206,10 +219,14 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int nrb = (m_end - m0 + 31) / 32;
     const int mba = min(MB, (nrb - wm + WM - 1) / WM);
 
-    // ---- per-lane DMA source offsets (32-bit; bases are wave-uniform),
-    // starting at this split's K range
+    // ---- per-lane DMA source offsets (32-bit; bases are wave-uniform, and
+    // 64-bit), starting at this split's K range.  Gathered token rows can be
+    // anywhere in x: their base is x (the host keeps x below 4 GiB).  Other
+    // token rows (x_perm, H, the router's x) are contiguous: their base is
+    // the tile's first row, so no offset exceeds 256 rows.
     const uint32_t k_base = (uint32_t)(tsplit * nK * RB);
-    const char* a_base = (const char*)g.a;
+    const bool gather = (MODE == 1 && g.perm != nullptr);
+    const char* a_base = (const char*)g.a + (gather ? 0 : (size_t)(row0 + m0) * row_bytes);
     uint32_t a_off[A_PW];
 #pragma unroll
     for (int q = 0; q < A_PW; ++q) {
@@ -217,11 +234,11 @@ grouped_gemm_big_kernel(GemmArgs g) {
       int rr = m0 + r;
       if (rr > m_end - 1) rr = m_end - 1;
       long src_row;
-      if (MODE == 1 && g.perm != nullptr) {
+      if (gather) {
         src_row = g.perm[row0 + rr] / g.top_k;  // gather token rows on load
         if (src_row < 0 || src_row >= g.M) src_row = 0;
       } else {
-        src_row = row0 + rr;
+        src_row = rr - m0;
       }
       a_off[q] = (uint32_t)(src_row * row_bytes) + k_base + swz(r, dma_slot) * 16;
     }
@@ -532,9 +549,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
 #define MOE_BIG_MG 4
 #endif
 
-int big_grid() {
-  int grid = device_cu_count();  // one workgroup per CU (LDS bound)
-  grid -= grid % 8;
+int big_grid(hipStream_t st) {
+  int grid = st == nullptr ? device_cu_count() : stream_cu_count(st);  // one workgroup per CU
+  grid -= grid % 8;                                                    // (LDS bound)
   return grid < 8 ? 8 : grid;
 }
 
@@ -542,7 +559,7 @@ template <int MODE>
 static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
   auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG>;
   if (device_cu_count() <= 0) return MOE_EHIP;
-  hipLaunchKernelGGL(kern, dim3(big_grid()), dim3(512), 0, st, g);
+  hipLaunchKernelGGL(kern, dim3(big_grid(st)), dim3(512), 0, st, g);
   return check_launch();
 }
 

@@ -30,15 +30,11 @@ int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st)
 
 // bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles
 // (K a multiple of 128, at most 1024 groups, at most 128 tiles per
-// workgroup of the big_grid() launched).
+// workgroup of the big_grid() launched: plan::ffn_use_big).
 constexpr int kBigTileRows = 256;
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st);
-int big_grid();
-
-// Upper bound on the m-tiles of ngroups groups holding rows rows in total.
-inline long big_tile_list_max(long rows, int ngroups) {
-  return rows / kBigTileRows + ngroups;
-}
+// Workgroups of a many-row launch on stream st (one per CU it may use).
+int big_grid(hipStream_t st);
 
 // partials: nsplit slices of [T, E] fp32 summed in slice order, plus
 // col_bias (nullable); logits_out (nullable) receives the sum.
@@ -77,7 +73,18 @@ int launch_pid(const int32_t* counts, int n_ffn, int T, float setpoint, float kp
 int launch_balance(const int32_t* counts, int n_ffn, float gamma, float* bias, hipStream_t st);
 
 int device_cu_count();
+int stream_cu_count(hipStream_t st);
 int check_launch();
+// Records a HIP error for moe_strerror (this thread).
+void set_hip_error(hipError_t e);
+
+// moe_dispatch's argument checks (no workspace) and its launches with the
+// per-block histogram `hist` ([E, dispatch_blocks(T*k)] int32).
+int dispatch_checks(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* counts,
+                    int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm);
+int dispatch_run(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv_perm, void* x_perm, int32_t* hist,
+                 hipStream_t st);
 
 // Number of blocks the dispatch kernels split T*k assignments into.
 inline int dispatch_blocks(long Tk) {

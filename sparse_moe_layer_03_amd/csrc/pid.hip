@@ -15,6 +15,13 @@
 #include "common.h"
 #include "internal.h"
 
+// Device code is compiled with FP contraction on, and HIP's __fmul_rn /
+// __fadd_rn are plain operators defined in a header (their operations carry
+// the header's contraction setting into any caller): the compiler fused
+// kp*err + ki*I into one FMA (one rounding instead of two).  So this file
+// turns contraction off and writes every operation as a plain operator.
+#pragma clang fp contract(off)
+
 namespace moe {
 
 __global__ void __launch_bounds__(64)
@@ -31,12 +38,13 @@ pid_kernel(const int32_t* __restrict__ counts, int n_ffn, int T, float setpoint,
     if (lane == 0) state->flags |= 1;
     return;
   }
-  const float r = __fdiv_rn((float)a, (float)T);
-  const float err = __fsub_rn(setpoint, r);
-  const float I = __fadd_rn(integral, err);
-  const float D = (step == 0) ? 0.f : __fsub_rn(err, prev);
-  const float delta = __fadd_rn(__fadd_rn(__fmul_rn(kp, err), __fmul_rn(ki, I)), __fmul_rn(kd, D));
-  for (int e = lane; e < n_ffn; e += 64) bias[e] = __fadd_rn(bias[e], delta);
+  const float r = (float)a / (float)T;
+  const float err = setpoint - r;
+  const float I = integral + err;
+  const float D = (step == 0) ? 0.f : err - prev;
+  const float p_term = kp * err, i_term = ki * I, d_term = kd * D;
+  const float delta = (p_term + i_term) + d_term;
+  for (int e = lane; e < n_ffn; e += 64) bias[e] = bias[e] + delta;
   if (lane == 0) {
     if (r_log != nullptr && step >= 0 && step < r_log_len) r_log[step] = r;
     state->integral = I;
@@ -81,8 +89,9 @@ balance_kernel(const int32_t* __restrict__ counts, int n_ffn, float gamma,
   for (int e = lane; e < n_ffn; e += 64) {
     const long d = (long)a - (long)n_ffn * counts[e];
     const int s = (d > 0) - (d < 0);
-    const float frac = __fdiv_rn((float)(n_ffn * s - ssum), (float)n_ffn);
-    bias[e] = __fadd_rn(bias[e], __fmul_rn(gamma, frac));
+    const float frac = (float)(n_ffn * s - ssum) / (float)n_ffn;
+    const float step = gamma * frac;
+    bias[e] = bias[e] + step;
   }
 }
 

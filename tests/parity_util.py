@@ -142,6 +142,64 @@ def oracle_outputs_for_tokens(m: Model, x_dev, tokens, gpu_idx):
     return O.combine(xs, yp, idx2, gate, d["inv_perm"], nU)
 
 
+def many_row_mtiles(offsets, n_ffn):
+    """Sorted-position ranges [lo, hi) of the m-tiles the many-row expert
+    GEMM cuts: expert e's c rows get ceil(c / 256) tiles of equal height,
+    rounded up to a multiple of 32 rows (the last tile takes the rest)."""
+    tiles = []
+    for e in range(n_ffn):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        c = hi - lo
+        if c == 0:
+            continue
+        mt = -(-c // 256)
+        h = -(-(-(-c // mt)) // 32) * 32
+        for i in range(mt):
+            a, b = lo + i * h, min(hi, lo + (i + 1) * h)
+            if a < b:
+                tiles.append((e, a, b))
+    return tiles
+
+
+def covering_tokens(gpu, n_ffn, top_k, n_min, seed=0, n_block_experts=16):
+    """Tokens whose FFN rows hit every m-tile of the expert GEMMs (a random
+    row and the last row of each), every 32-row block of the last eight
+    touched experts (the tiles of the persistent grid's last round) and of
+    eight random touched experts, topped up with random tokens to n_min.
+    Returns (sorted tokens, m-tiles, sampled positions)."""
+    rng = np.random.default_rng(seed)
+    off = gpu["offsets"]
+    perm = gpu["perm"]
+    tiles = many_row_mtiles(off, n_ffn)
+    pos = set()
+    for _, a, b in tiles:
+        pos.add(int(rng.integers(a, b)))
+        pos.add(b - 1)
+    touched = [e for e in range(n_ffn) if off[e + 1] > off[e]]
+    extra = list(touched[-(n_block_experts // 2):])
+    rest = [e for e in touched if e not in extra]
+    if rest:
+        extra += list(rng.choice(rest, min(len(rest), n_block_experts // 2), replace=False))
+    for e in extra:
+        lo, hi = int(off[e]), int(off[e + 1])
+        for a in range(lo, hi, 32):
+            pos.add(int(rng.integers(a, min(hi, a + 32))))
+    toks = set(int(perm[p]) // top_k for p in pos)
+    T = gpu["topk_idx"].shape[0]
+    if len(toks) < n_min:
+        others = np.setdiff1d(np.arange(T), np.fromiter(toks, int))
+        toks |= set(int(t) for t in rng.choice(others, min(len(others), n_min - len(toks)),
+                                                   replace=False))
+    toks = np.array(sorted(toks))
+    # every m-tile holds a row of a sampled token
+    inv = gpu["inv_perm"].reshape(T, top_k)
+    hit = np.sort(inv[toks].ravel())
+    for e, a, b in tiles:
+        i = np.searchsorted(hit, a)
+        assert i < hit.size and hit[i] < b, f"m-tile {a}:{b} of expert {e} not covered"
+    return toks, tiles, pos
+
+
 def full_oracle(m: Model, x_dev, gpu_idx=None):
     w = m.w
     return O.forward(S.to_numpy64(x_dev), S.to_numpy64(m.wr), m.bias.cpu().numpy(),

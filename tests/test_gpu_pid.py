@@ -1,6 +1,8 @@
-"""GPU PID loop: the bias after every batch equals the oracle's PID fed the
-GPU's per-batch counts, the trajectory reaches the set point, and a
-checkpoint/resume of the device state reproduces the run bit for bit."""
+"""GPU PID loop: the bias and controller state after every batch equal, bit
+for bit, the oracle's float32 PID fed the GPU's per-batch counts (and lie
+within float32 rounding of its float64 evaluation); the trajectory reaches
+the set point; a checkpoint/resume of the device state reproduces the run
+bit for bit."""
 
 import json
 import os
@@ -28,7 +30,9 @@ def run_pid_loop(w, batches, m=None, buf=None, start=0, check_every=None):
     params = B.MoePidParams(*w.pid)
     r_log = torch.full((start + batches,), -1.0, dtype=torch.float32, device="cuda")
     bias_o = m.bias.cpu().numpy().astype(np.float64)
+    bias_32 = m.bias.cpu().numpy().astype(np.float32)
     st = B_state_to_oracle(buf.pid_state)
+    st32 = B_state_to_oracle(buf.pid_state)
     rs, loads = [], []
     for b in range(start, start + batches):
         x = S.make_x(w, b, "cuda")
@@ -41,12 +45,22 @@ def run_pid_loop(w, batches, m=None, buf=None, start=0, check_every=None):
                          r_log.numel())
         counts = buf.counts.cpu().numpy()
         bias_o, st, r_o = O.pid_update(counts, w.n_ffn, w.T, bias_o, st, *w.pid)
-        np.testing.assert_allclose(m.bias.cpu().numpy(), bias_o, rtol=2e-6, atol=2e-7)
+        bias_32, st32, r_32 = O.pid_update_f32(counts, w.n_ffn, w.T, bias_32, st32, *w.pid)
+        g_bias = m.bias.cpu().numpy()
+        # bit for bit against the float32 controller ...
+        np.testing.assert_array_equal(g_bias.view(np.int32), bias_32.view(np.int32))
+        g_st = B_state_to_oracle(buf.pid_state)
+        assert (np.float32(g_st.integral).view(np.int32), np.float32(g_st.prev_err).view(np.int32),
+                g_st.step) == (np.float32(st32.integral).view(np.int32),
+                               np.float32(st32.prev_err).view(np.int32), st32.step)
+        # ... and within float32 rounding of the float64 law
+        np.testing.assert_allclose(g_bias, bias_o, rtol=2e-6, atol=2e-7)
         rs.append(r_o)
         loads.append(counts[:w.n_ffn].var())
     torch.cuda.synchronize()
     r_gpu = r_log.cpu().numpy()[start:]
     np.testing.assert_array_equal(r_gpu, np.float32(np.array(rs)))
+    say(f"  bias and state bit-exact against the float32 oracle PID over {batches} batches")
     return np.array(rs), np.array(loads), m, buf
 
 
