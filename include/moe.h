@@ -144,6 +144,22 @@ int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
                  int32_t* perm, int32_t* inv_perm, void* x_perm, void* ws,
                  void* stream);
 
+/* moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments
+ * (minus ws), kernels and results as moe_dispatch.  Its scratch -- the
+ * per-block expert histogram, E * ceil(T*top_k / 1024) int32 (blocks capped
+ * at 256), at most 1 MiB -- is a static device array of the library, one
+ * per device, held until the process ends; it needs no clearing.  Every
+ * call on a device shares that device's array, so calls that overlap on one
+ * device (two streams or threads) race on it: serialise them.  A shape whose
+ * histogram exceeds 1 MiB returns MOE_EUNSUPPORTED (none within the limits
+ * above does).  Allocates nothing: no hipMalloc, no hipFree. */
+int moe_dispatch_noalloc(const moe_shape* shape, const int32_t* topk_idx,
+                         const void* x, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* inv_perm, void* x_perm,
+                         void* stream);
+
 /* moe_expert_ffn -- every FFN expert e < n_ffn on its rows
  * [offsets[e], offsets[e+1]) ([DS] expert width; activation read as SwiGLU):
  *   H = silu(X W_gate[e]^T) * (X W_up[e]^T),  y_perm rows = H W_down[e]^T,

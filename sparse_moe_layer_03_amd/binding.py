@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP",
 # every entry point declared in include/moe.h
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_strerror", "moe_device_cu_count", "moe_route",
                 "moe_dispatch", "moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                "moe_combine", "moe_pid_update", "moe_balance_update")
+                "moe_combine", "moe_pid_update", "moe_balance_update", "moe_dispatch_noalloc")
 
 
 class MoeShape(ctypes.Structure):
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [sp] + [vp] * 7
         L.moe_pid_update.argtypes = [sp, ctypes.POINTER(MoePidParams), vp, vp, vp, vp, i32, vp]
         L.moe_balance_update.argtypes = [sp, ctypes.c_float, vp, vp, vp]
+        L.moe_dispatch_noalloc.argtypes = [sp] + [vp] * 8
         for n in ENTRY_POINTS[3:]:
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -120,6 +121,14 @@ def moe_dispatch(shape, topk_idx, x, counts, offsets, perm, inv_perm, x_perm, ws
     _check("moe_dispatch", lib().moe_dispatch(ctypes.byref(shape), _p(topk_idx), _p(x),
                                               _p(counts), _p(offsets), _p(perm), _p(inv_perm),
                                               _p(x_perm), _p(ws), _stream(stream)))
+
+
+def moe_dispatch_noalloc(shape, topk_idx, x, counts, offsets, perm, inv_perm, x_perm,
+                         stream=None):
+    _check("moe_dispatch_noalloc",
+           lib().moe_dispatch_noalloc(ctypes.byref(shape), _p(topk_idx), _p(x), _p(counts),
+                                      _p(offsets), _p(perm), _p(inv_perm), _p(x_perm),
+                                      _stream(stream)))
 
 
 def moe_expert_ffn(shape, x, x_perm, perm, offsets, w_gate, w_up, w_down, y_perm, ws,

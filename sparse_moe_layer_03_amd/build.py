@@ -17,7 +17,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "gemm.hip", "gemm_big.hip", "route.hip", "dispatch.hip", "combine.hip", "pid.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemm_big.hip", "route.hip", "dispatch.hip", "combine.hip", "pid.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

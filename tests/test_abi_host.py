@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(B.ENTRY_POINTS)
     L = B.lib()
     for n in names:
