@@ -356,25 +356,15 @@ grouped_gemm_big_kernel(GemmArgs g) {
           bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * RB + (swz(r, c) << 4)]);
         }
       };
-      // DMA pieces of slice kk: A loads 2kk, 2kk+1 (kk < 2), B loads 2(kk-2), 2(kk-2)+1.
-      // In the main loop a wave with MBA active 32-row blocks issues only its
-      // token-row loads q < MBA: load q of wave w fills tile rows 64q + 8w +
-      // [0, 8), and a row in an active block of any wave (block 2i + wm, i <
-      // mba(wm)) lies in a load q < mba of a wave of the same wm half, so
-      // every row an MFMA reads is filled.  Rows of inactive blocks keep
-      // stale data; only the tail steps read them, into blocks never stored.
-      // The step-start vmcnt wait stays valid: it lets the last B_PW loads
-      // (the weights issued after the token rows) stay in flight, and fewer
-      // token-row loads only make it pass sooner.
+      // DMA pieces of slice kk: A loads 2kk, 2kk+1 (kk < 2), B loads 2(kk-2), 2(kk-2)+1
       auto dma_piece = [&](int kk) {
         if (kk < 2) {
           char* sa2 = stage_a(std::integral_constant<int, (AS + 1) % 2>{});
           const size_t off = (size_t)(ks + 1) * RB;
 #pragma unroll
           for (int q = 2 * kk; q < 2 * kk + 2; ++q)
-            if (q < MBA)  // token-row load q fills rows [64q, 64q + 64): see below
-              __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
-                                               (lds_void_t*)(sa2 + (wave + q * NW) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
+                                             (lds_void_t*)(sa2 + (wave + q * NW) * 1024), 16, 0, 0);
         } else {
           char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
           const size_t off = (size_t)(ks + 2) * RB;
