@@ -87,6 +87,17 @@ def parse():
                     help="shortcut-connected block: time the MoE layer against a dense "
                          "SwiGLU branch of this width on a second stream (e.g. 12288); "
                          "0 = off")
+    ap.add_argument("--cu-split", default="",
+                    help="with --scmoe: comma-separated CU counts for the dense branch; for "
+                         "each, the MoE layer and the branch run on CU-masked streams with "
+                         "disjoint CU sets (the layer gets the rest; contiguous CU ranges, the "
+                         "masks the runtime accepts)")
+    ap.add_argument("--eplb", default="",
+                    help="SLOTS,DEVICES: after each batch's dispatch, plan the placement of "
+                         "the FFN experts on SLOTS expert slots over DEVICES devices of an EP "
+                         "domain (moe_eplb_plan) and report each batch's device max/mean load: "
+                         "one expert per slot, the plan of the same batch, and the plan of the "
+                         "previous batch applied to it")
     ap.add_argument("--balance", type=float, default=0.0,
                     help="per-expert load-balancing step (moe_balance_update) after the PID; "
                          "0 = off")
@@ -295,13 +306,45 @@ def scmoe_main(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / args.steps * 1e3
 
+    # CU-partitioned variants: the layer and the branch on CU-masked streams
+    # with disjoint CU sets (default priority)
+    masked = {}
+    n_cus = B.moe_device_cu_count()
+    for part in [int(v) for v in args.cu_split.split(",") if v.strip()]:
+        for pattern in ("contiguous",):
+            d_words = scmoe.cu_mask(n_cus, 0, part, pattern)
+            m_words = [(~v) & 0xFFFFFFFF for v in d_words]
+            if n_cus % 32:
+                m_words[-1] &= (1 << (n_cus % 32)) - 1
+            masked[f"{pattern}_dense{part}"] = (scmoe.MaskedStream(m_words),
+                                                scmoe.MaskedStream(d_words))
+
+    def masked_concurrent(key):
+        ms_, ds_ = masked[key]
+
+        def fn():
+            ms_.stream.wait_stream(main_s)
+            ds_.stream.wait_stream(main_s)
+            with torch.cuda.stream(ms_.stream):
+                B.layer_forward(buf, x, wr, bias, wg, wu, wd, stream=ms_.stream)
+            with torch.cuda.stream(ds_.stream):
+                br.run(x, w1, w3, w2, stream=ds_.stream)
+            main_s.wait_stream(ms_.stream)
+            main_s.wait_stream(ds_.stream)
+        return fn
+
     # interleave the modes over three rounds; keep each mode's best round
-    res = {k: [] for k in ("moe", "dense", "serial", "concurrent")}
+    res = {k: [] for k in ["moe", "dense", "serial", "concurrent"] + list(masked)}
     for _ in range(3):
         res["moe"].append(timed(moe))
         res["dense"].append(timed(dense))
         res["serial"].append(timed(both_serial))
         res["concurrent"].append(timed(both_concurrent))
+        for key in masked:
+            res[key].append(timed(masked_concurrent(key)))
+    for ms_, ds_ in masked.values():
+        ms_.close()
+        ds_.close()
     ms = {k: float(np.min(v)) for k, v in res.items()}
     dense_flops = 6.0 * w.T * w.d_model * args.scmoe
     line = {
@@ -327,9 +370,51 @@ def scmoe_main(args):
                   "dense_weight_gb_per_s": 3.0 * w.d_model * args.scmoe
                   * (2 if w.dtype == "bf16" else 4) / (ms["dense"] * 1e-3) / 1e9,
                   "dense_tflop_per_s": dense_flops / (ms["dense"] * 1e-3) / 1e12,
+                  "cu_partitioned_ms": {k: ms[k] for k in masked},
                   "rounds_ms": res},
     }
     print(json.dumps(line), flush=True)
+
+
+def eplb_report(w, loads, eplb, dispatch_ms):
+    """Per-batch device max/mean FFN load of the expert placement plans
+    (counts of each batch from the load log): experts one per slot in id
+    order (expert e on device e * D // N), the plan made from the same
+    batch, and the plan of the previous batch applied to this batch's
+    counts (each expert's rows split over its replicas as the plan does)."""
+    import numpy as np
+
+    D = eplb["D"]
+    rep = eplb["rep"].cpu().numpy()
+    sdev = eplb["sdev"].cpu().numpy()
+    dload = eplb["dload"].cpu().numpy().astype(np.int64)
+    N = w.n_ffn
+
+    def ratio(v):
+        v = np.asarray(v, np.float64)
+        return round(float(v.max() / max(v.mean(), 1e-12)), 3)
+
+    def apply(counts, r, devs):
+        out = np.zeros(D, np.int64)
+        s = 0
+        for e in range(N):
+            c = int(counts[e])
+            for j in range(int(r[e])):
+                out[devs[s]] += (j + 1) * c // int(r[e]) - j * c // int(r[e])
+                s += 1
+        return out
+
+    K = loads.shape[0]
+    naive = [ratio(np.bincount(np.arange(N) * D // N, weights=loads[i, :N], minlength=D))
+             for i in range(K)]
+    same = [ratio(dload[i]) for i in range(K)]
+    prev = [None] + [ratio(apply(loads[i, :N], rep[i - 1], sdev[i - 1])) for i in range(1, K)]
+    return {"slots": eplb["S"], "devices": D,
+            "device_max_over_mean_one_expert_per_slot": naive,
+            "device_max_over_mean_planned_same_batch": same,
+            "device_max_over_mean_planned_previous_batch": prev,
+            "dispatch_plus_plan_ms_mean": float(np.mean(dispatch_ms)),
+            "replicas_of_the_hottest_expert_last_batch": int(rep[K - 1].max())}
 
 
 def build_model(w, dev):
@@ -389,6 +474,16 @@ def run_workload(w, args, mdl, dev, cpu=True):
     r_log = torch.zeros(max(args.steps, 1) + args.warmup + 1, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     load_log = None
+    eplb = None
+    if args.eplb:
+        n_slots, n_dev = (int(v) for v in args.eplb.split(","))
+        i32 = dict(dtype=torch.int32, device=dev)
+        Kp = max(args.steps, 1)
+        eplb = dict(S=n_slots, D=n_dev, rep=torch.zeros((Kp, w.n_ffn), **i32),
+                    sexp=torch.zeros((Kp, n_slots), **i32),
+                    srows=torch.zeros((Kp, n_slots, 2), **i32),
+                    sdev=torch.zeros((Kp, n_slots), **i32),
+                    dload=torch.zeros((Kp, n_dev), **i32))
 
     def step(i, ev=None):
         """One step; ev: None, 7 events (every stage boundary) or 4 events
@@ -403,6 +498,11 @@ def run_workload(w, args, mdl, dev, cpu=True):
             ev[1].record(stream)
         B.moe_dispatch(shape, buf.topk_idx, x, buf.counts, buf.offsets, buf.perm,
                        buf.inv_perm, None, buf.ws)
+        if eplb is not None:
+            j = i % eplb["rep"].shape[0]
+            B.moe_eplb_plan(shape, eplb["S"], eplb["D"], buf.counts, buf.offsets,
+                            eplb["rep"][j], eplb["sexp"][j], eplb["srows"][j], eplb["sdev"][j],
+                            eplb["dload"][j])
         if ev is not None:
             ev[2 if full else 1].record(stream)
         B.moe_ffn_gate_up(shape, x, None, buf.perm, buf.offsets, wg, wu, buf.ws)
@@ -596,6 +696,8 @@ def run_workload(w, args, mdl, dev, cpu=True):
         line["ffn_load_variance_per_step"] = [round(float(r.var()), 1) for r in ll]
     if args.balance > 0:
         line["balance_gamma"] = args.balance
+    if eplb is not None:
+        line["eplb"] = eplb_report(w, loads, eplb, st_ms["dispatch"])
 
     line["cpu_baseline"] = None
     if cpu and not args.no_cpu_baseline:

@@ -221,6 +221,32 @@ int moe_pid_update(const moe_shape* shape, const moe_pid_params* pid_params,
 int moe_balance_update(const moe_shape* shape, float gamma, const int32_t* counts,
                        float* bias, void* stream);
 
+/* moe_eplb_plan -- expert placement balancing over an expert-parallel
+ * domain (Ascend deployment article, section "MoE专家动态负载均衡": with a
+ * very large EP domain the tokens each expert receives vary widely, and
+ * dynamic load balancing narrows the gap between experts' loads).  Routing
+ * is untouched: the plan says where FFN experts' rows are computed.
+ * The n_ffn experts occupy n_slots expert slots on n_devices devices
+ * (n_slots / n_devices each):
+ *   replicas[e] >= 1, sum = n_slots: each redundant slot goes, one at a
+ *     time, to the expert with the most tokens per replica (largest
+ *     counts[e] / replicas[e], exact; ties to the lower id);
+ *   slots in expert order: slot_expert[s]; replica j of expert e (c rows,
+ *     r replicas) takes sorted positions slot_rows[2s] .. slot_rows[2s+1]
+ *     = offsets[e] + j*c/r .. offsets[e] + (j+1)*c/r (integer division);
+ *   slot_device[s]: longest first (slot loads descending, ties to the lower
+ *     slot), each to the least-loaded device with room (ties to the lower
+ *     device); device_load[d] = rows placed on device d.
+ *   counts [>= n_ffn] int32, offsets [>= n_ffn + 1] int32 (moe_dispatch);
+ *   replicas [n_ffn], slot_expert [n_slots], slot_rows [n_slots, 2],
+ *   slot_device [n_slots], device_load [n_devices]: int32 outputs.
+ * Limits: n_ffn <= n_slots <= 4096, 1 <= n_devices <= 64, n_devices divides
+ * n_slots (else MOE_EINVAL / MOE_EUNSUPPORTED).  One workgroup. */
+int moe_eplb_plan(const moe_shape* shape, int32_t n_slots, int32_t n_devices,
+                  const int32_t* counts, const int32_t* offsets, int32_t* replicas,
+                  int32_t* slot_expert, int32_t* slot_rows, int32_t* slot_device,
+                  int32_t* device_load, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

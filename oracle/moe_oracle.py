@@ -55,6 +55,14 @@ Readings where the pages are silent (each is listed in the design notes):
   balancing narrows the gap between experts' token loads; method not
   stated): a zero-sum sign step on the FFN experts' correction bias, so it
   evens the load without moving the mean FFN bias the PID controls.
+* The same passage read as placement balancing across the expert-parallel
+  domain (it names the very large EP domain as the cause of the load
+  variance, and an inference deployment cannot change which experts a token
+  picks): the N FFN experts occupy S >= N expert slots on D devices; each
+  redundant slot replicates the expert with the most tokens per replica, an
+  expert's rows are split evenly over its replicas, and slots go to devices
+  by longest-processing-time-first with S / D slots per device.  Routing,
+  and so the PID's budget, is untouched.
 """
 
 from __future__ import annotations
@@ -78,6 +86,11 @@ __all__ = [
     "pid_update",
     "pid_update_f32",
     "balance_update",
+    "eplb_replicas",
+    "eplb_slots",
+    "eplb_place",
+    "eplb_plan",
+    "eplb_device_loads",
     "forward",
 ]
 
@@ -349,6 +362,86 @@ def balance_update(counts, n_ffn, bias, gamma):
     new_bias = _f64(bias).copy()
     new_bias[:n_ffn] += delta
     return new_bias
+
+
+# ------------------------------------------ expert placement balancing ----
+
+def eplb_replicas(counts, n_ffn, n_slots):
+    """Replicas per FFN expert for n_slots >= n_ffn expert slots.
+
+    Every expert holds one slot; each of the n_slots - n_ffn redundant slots
+    goes, one at a time, to the expert with the most tokens per replica
+    (largest c_e / r_e, compared exactly; ties to the lower id).  [AS]
+    "MoE专家动态负载均衡": the per-expert token load varies widely across the
+    EP domain and dynamic balancing narrows the gap.
+    """
+    c = [int(v) for v in np.asarray(counts)[:n_ffn]]
+    r = [1] * n_ffn
+    for _ in range(n_slots - n_ffn):
+        best = 0
+        for e in range(1, n_ffn):
+            if c[e] * r[best] > c[best] * r[e]:   # c_e / r_e > c_best / r_best
+                best = e
+        r[best] += 1
+    return np.array(r, dtype=np.int32)
+
+
+def eplb_slots(counts, replicas, offsets=None):
+    """Slots in expert order (slot s = replica j of expert e, experts
+    ascending, replicas ascending).  Replica j of an expert with c rows and
+    r replicas takes rows [j*c // r, (j+1)*c // r) of its segment (absolute
+    sorted positions when offsets are given).  Returns (expert, begin, end)
+    int arrays of length sum(replicas)."""
+    ex, beg, end = [], [], []
+    for e, r in enumerate(np.asarray(replicas)):
+        c = int(counts[e])
+        base = 0 if offsets is None else int(offsets[e])
+        for j in range(int(r)):
+            ex.append(e)
+            beg.append(base + (j * c) // int(r))
+            end.append(base + ((j + 1) * c) // int(r))
+    return (np.array(ex, np.int32), np.array(beg, np.int32), np.array(end, np.int32))
+
+
+def eplb_place(slot_loads, n_devices):
+    """Longest processing time first with equal capacity: slots in order of
+    load descending (ties to the lower slot), each to the least-loaded device
+    that still has room for one of its len / n_devices slots (ties to the
+    lower device).  Returns (device per slot, load per device)."""
+    loads = [int(v) for v in slot_loads]
+    S = len(loads)
+    cap = S // n_devices
+    order = sorted(range(S), key=lambda i: (-loads[i], i))
+    dev = [0] * S
+    dload = [0] * n_devices
+    used = [0] * n_devices
+    for i in order:
+        best = -1
+        for d in range(n_devices):
+            if used[d] < cap and (best < 0 or dload[d] < dload[best]):
+                best = d
+        dev[i] = best
+        dload[best] += loads[i]
+        used[best] += 1
+    return np.array(dev, np.int32), np.array(dload, np.int64)
+
+
+def eplb_plan(counts, offsets, n_ffn, n_slots, n_devices):
+    """Replicas, slots and placement of one batch's FFN loads (see above)."""
+    rep = eplb_replicas(counts, n_ffn, n_slots)
+    ex, beg, end = eplb_slots(counts, rep, offsets)
+    dev, dload = eplb_place(end - beg, n_devices)
+    return dict(replicas=rep, slot_expert=ex, slot_begin=beg, slot_end=end,
+                slot_device=dev, device_load=dload)
+
+
+def eplb_device_loads(counts, replicas, slot_device, n_devices):
+    """Device loads of a placement applied to (possibly other) counts: each
+    expert's rows split over its replicas as in eplb_slots."""
+    ex, beg, end = eplb_slots(counts, replicas)
+    out = np.zeros(n_devices, np.int64)
+    np.add.at(out, np.asarray(slot_device), (end - beg).astype(np.int64))
+    return out
 
 
 # --------------------------------------------------------------- forward ----

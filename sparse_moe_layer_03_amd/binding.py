@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP",
 # every entry point declared in include/moe.h
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_strerror", "moe_device_cu_count", "moe_route",
                 "moe_dispatch", "moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                "moe_combine", "moe_pid_update", "moe_balance_update", "moe_dispatch_noalloc")
+                "moe_combine", "moe_pid_update", "moe_balance_update", "moe_dispatch_noalloc",
+                "moe_eplb_plan")
 
 
 class MoeShape(ctypes.Structure):
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.moe_pid_update.argtypes = [sp, ctypes.POINTER(MoePidParams), vp, vp, vp, vp, i32, vp]
         L.moe_balance_update.argtypes = [sp, ctypes.c_float, vp, vp, vp]
         L.moe_dispatch_noalloc.argtypes = [sp] + [vp] * 8
+        L.moe_eplb_plan.argtypes = [sp, i32, i32] + [vp] * 8
         for n in ENTRY_POINTS[3:]:
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -165,6 +167,14 @@ def moe_pid_update(shape, params: MoePidParams, counts, state, bias, r_log=None,
 def moe_balance_update(shape, gamma, counts, bias, stream=None):
     _check("moe_balance_update", lib().moe_balance_update(ctypes.byref(shape), float(gamma),
                                                           _p(counts), _p(bias), _stream(stream)))
+
+
+def moe_eplb_plan(shape, n_slots, n_devices, counts, offsets, replicas, slot_expert, slot_rows,
+                  slot_device, device_load, stream=None):
+    _check("moe_eplb_plan",
+           lib().moe_eplb_plan(ctypes.byref(shape), int(n_slots), int(n_devices), _p(counts),
+                               _p(offsets), _p(replicas), _p(slot_expert), _p(slot_rows),
+                               _p(slot_device), _p(device_load), _stream(stream)))
 
 
 class LayerBuffers:

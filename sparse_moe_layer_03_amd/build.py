@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libmoe_mi355x.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "gemm.hip", "gemm_big.hip", "route.hip", "dispatch.hip", "combine.hip", "pid.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "eplb.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -348,4 +348,21 @@ int moe_balance_update(const moe_shape* s, float gamma, const int32_t* counts, f
   return launch_balance(counts, s->n_ffn, gamma, bias, (hipStream_t)stream);
 }
 
+int moe_eplb_plan(const moe_shape* s, int32_t n_slots, int32_t n_devices, const int32_t* counts,
+                  const int32_t* offsets, int32_t* replicas, int32_t* slot_expert,
+                  int32_t* slot_rows, int32_t* slot_device, int32_t* device_load, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!counts || !offsets || !replicas || !slot_expert || !slot_rows || !slot_device ||
+      !device_load)
+    return MOE_EINVAL;
+  if (n_devices < 1 || n_slots < s->n_ffn || n_slots % n_devices != 0) return MOE_EINVAL;
+  if (n_slots > kEplbMaxSlots || n_devices > kEplbMaxDevices) return MOE_EUNSUPPORTED;
+  if (!al4(counts) || !al4(offsets) || !al4(replicas) || !al4(slot_expert) || !al4(slot_rows) ||
+      !al4(slot_device) || !al4(device_load))
+    return MOE_EALIGN;
+  return launch_eplb(counts, offsets, s->n_ffn, n_slots, n_devices, replicas, slot_expert,
+                     slot_rows, slot_device, device_load, (hipStream_t)stream);
+}
+
 }  // extern "C"

@@ -72,6 +72,14 @@ int launch_pid(const int32_t* counts, int n_ffn, int T, float setpoint, float kp
 
 int launch_balance(const int32_t* counts, int n_ffn, float gamma, float* bias, hipStream_t st);
 
+// Expert placement over an EP domain: at most 4096 slots on at most 64
+// devices (one workgroup; slot keys sorted in 32 KiB of LDS).
+constexpr int kEplbMaxSlots = 4096;
+constexpr int kEplbMaxDevices = 64;
+int launch_eplb(const int32_t* counts, const int32_t* offsets, int n_ffn, int n_slots,
+                int n_devices, int32_t* replicas, int32_t* slot_expert, int32_t* slot_rows,
+                int32_t* slot_device, int32_t* device_load, hipStream_t st);
+
 int device_cu_count();
 int stream_cu_count(hipStream_t st);
 int check_launch();

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(B.ENTRY_POINTS)
     L = B.lib()
     for n in names:
@@ -90,3 +90,18 @@ def test_pid_rejects_nonfinite_params():
         assert L.moe_pid_update(ctypes.byref(s), ctypes.byref(bad), a, a, a, None, 0, None) == -4
     ok = B.MoePidParams(6.0, 0.01, 0.001, 0.0)
     assert L.moe_pid_update(ctypes.byref(s), ctypes.byref(ok), None, a, a, None, 0, None) == -1
+
+
+def test_eplb_plan_rejects_bad_slot_and_device_counts():
+    s = B.make_shape(64, 128, 8, 4, 256, 2, "bf16")
+    L = B.lib()
+    a = ctypes.c_void_p(0x1000)
+    args = [a] * 7 + [None]
+    assert L.moe_eplb_plan(ctypes.byref(s), 7, 1, *args) == -1      # fewer slots than experts
+    assert L.moe_eplb_plan(ctypes.byref(s), 12, 5, *args) == -1     # devices do not divide slots
+    assert L.moe_eplb_plan(ctypes.byref(s), 12, 0, *args) == -1     # no device
+    assert L.moe_eplb_plan(ctypes.byref(s), 8192, 8, *args) == -2   # more than 4096 slots
+    assert L.moe_eplb_plan(ctypes.byref(s), 128, 128, *args) == -2  # more than 64 devices
+    assert L.moe_eplb_plan(ctypes.byref(s), 12, 4, None, *args[1:]) == -1
+    bad = ctypes.c_void_p(0x1002)
+    assert L.moe_eplb_plan(ctypes.byref(s), 12, 4, bad, *args[1:]) == -5

@@ -460,3 +460,88 @@ def test_balance_evens_a_two_expert_split():
         bias = O.balance_update(c, 2, bias, 0.01)
     assert shares[0] < 0.4
     assert abs(np.mean(shares[-20:]) - 0.5) < 0.05
+
+
+# ------------------------------------------- expert placement balancing ----
+
+def test_eplb_hand_worked_example():
+    with open(os.path.join(GOLDEN, "eplb_example.json")) as f:
+        g = json.load(f)
+    c = np.array(g["counts"])
+    off = np.concatenate([[0], np.cumsum(c)])
+    p = O.eplb_plan(c, off, len(c), g["n_slots"], g["n_devices"])
+    for k in ("replicas", "slot_expert", "slot_begin", "slot_end", "slot_device",
+              "device_load"):
+        assert p[k].tolist() == g["expected_" + k], k
+
+
+def _max_per_replica(c, r):
+    from fractions import Fraction
+    return max(Fraction(int(ci), int(ri)) for ci, ri in zip(c, r))
+
+
+def test_eplb_replicas_minimise_the_largest_per_replica_load():
+    # against every replica vector with r_e >= 1 and sum S (brute force)
+    rr = rng(80)
+    for _ in range(60):
+        N = int(rr.integers(1, 5))
+        S = N + int(rr.integers(0, 5))
+        c = rr.integers(0, 40, N)
+        best = min(_max_per_replica(c, r)
+                   for r in itertools.product(range(1, S - N + 2), repeat=N) if sum(r) == S)
+        got = O.eplb_replicas(c, N, S)
+        assert got.sum() == S and (got >= 1).all()
+        assert _max_per_replica(c, got) == best, (c, S, got)
+
+
+def test_eplb_slots_split_every_expert_evenly():
+    rr = rng(81)
+    c = rr.integers(0, 500, 40)
+    off = np.concatenate([[0], np.cumsum(c)])
+    rep = O.eplb_replicas(c, 40, 64)
+    ex, beg, end = O.eplb_slots(c, rep, off)
+    assert ex.size == 64 and (np.diff(ex) >= 0).all()
+    for e in range(40):
+        m = ex == e
+        assert m.sum() == rep[e]
+        assert beg[m][0] == off[e] and end[m][-1] == off[e + 1]           # whole segment
+        assert (beg[m][1:] == end[m][:-1]).all()                          # contiguous
+        sizes = end[m] - beg[m]
+        assert sizes.max() - sizes.min() <= 1                             # even split
+
+
+def test_eplb_placement_capacity_and_longest_first_bound():
+    # every device gets exactly S / D slots; the greedy's largest device load
+    # stays within 4/3 of the best placement found by brute force
+    rr = rng(82)
+    for _ in range(40):
+        D = int(rr.integers(2, 4))
+        S = D * int(rr.integers(1, 4))
+        loads = rr.integers(0, 30, S)
+        dev, dl = O.eplb_place(loads, D)
+        assert np.bincount(dev, minlength=D).tolist() == [S // D] * D
+        assert dl.sum() == loads.sum()
+        np.testing.assert_array_equal(np.bincount(dev, weights=loads, minlength=D), dl)
+        opt = None
+        for assign in itertools.product(range(D), repeat=S):
+            if np.bincount(assign, minlength=D).tolist() != [S // D] * D:
+                continue
+            m = np.bincount(assign, weights=loads, minlength=D).max()
+            opt = m if opt is None else min(opt, m)
+        assert dl.max() <= opt * 4 / 3 + 1e-9, (loads, dl, opt)
+
+
+def test_eplb_plan_leaves_routing_alone_and_narrows_the_device_gap():
+    # Zipf-like loads over 64 experts on 8 devices: 16 redundant slots cut
+    # the device max/mean load well below the naive one-expert-per-slot
+    # placement (experts e on device e // 8)
+    rr = rng(83)
+    q = 1.0 / np.arange(1, 65) ** 1.2
+    c = rr.multinomial(20000, q / q.sum())[rr.permutation(64)]
+    off = np.concatenate([[0], np.cumsum(c)])
+    p = O.eplb_plan(c, off, 64, 80, 8)
+    naive = np.add.reduceat(c, np.arange(0, 64, 8))
+    assert p["device_load"].sum() == c.sum() == naive.sum()
+    assert p["device_load"].max() / p["device_load"].mean() < 0.5 * naive.max() / naive.mean()
+    np.testing.assert_array_equal(
+        O.eplb_device_loads(c, p["replicas"], p["slot_device"], 8), p["device_load"])
