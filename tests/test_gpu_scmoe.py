@@ -85,3 +85,49 @@ def test_moe_and_dense_on_two_streams_match_serial():
         torch.cuda.synchronize()
         assert torch.equal(buf.y, y_moe), rep
         assert torch.equal(br.y, y_dense), rep
+
+
+@pytest.mark.parametrize("dense_cus,pattern", [(32, "contiguous"), (64, "contiguous")])
+def test_moe_and_dense_on_cu_partitioned_streams_match_serial(dense_cus, pattern):
+    # the MoE layer and the dense branch each on its own CU-masked stream
+    # (disjoint CU sets, default priority): outputs equal the serial run bit
+    # for bit, with persistent grids sized to each stream's share
+    w = S.Workload("scmoe_cu", T=2048, d_model=512, n_ffn=16, n_zero=8, d_ff=384, top_k=4,
+                   dtype="bf16", bias_var=0.01, seed=8)
+    say(f"MoE layer || dense branch on CU-partitioned streams ({dense_cus} CUs, {pattern})")
+    m = Model(w)
+    x = S.make_x(w, 0, "cuda")
+    w1, w3, w2 = S.make_dense(w, 1536, "cuda")
+    br = scmoe.DenseBranch(w.T, w.d_model, 1536, "bf16")
+    buf = B.LayerBuffers(m.shape, "cuda")
+    run_gpu(m, x, buf, with_logits=False)
+    y_dense = br.run(x, w1, w3, w2).clone()
+    torch.cuda.synchronize()
+    y_moe = buf.y.clone()
+
+    n = B.moe_device_cu_count()
+    d_words = scmoe.cu_mask(n, 0, dense_cus, pattern)
+    m_words = [(~v) & 0xFFFFFFFF for v in d_words]
+    if n % 32:
+        m_words[-1] &= (1 << (n % 32)) - 1
+    ms, ds = scmoe.MaskedStream(m_words), scmoe.MaskedStream(d_words)
+    try:
+        assert ms.cus == n - dense_cus and ds.cus == dense_cus
+        main = torch.cuda.current_stream()
+        for rep in range(3):
+            buf.y.zero_()
+            br.y.zero_()
+            ms.stream.wait_stream(main)
+            ds.stream.wait_stream(main)
+            with torch.cuda.stream(ms.stream):
+                B.layer_forward(buf, x, m.wr, m.bias, m.wg, m.wu, m.wd, stream=ms.stream)
+            with torch.cuda.stream(ds.stream):
+                br.run(x, w1, w3, w2, stream=ds.stream)
+            main.wait_stream(ms.stream)
+            main.wait_stream(ds.stream)
+            torch.cuda.synchronize()
+            assert torch.equal(buf.y, y_moe), rep
+            assert torch.equal(br.y, y_dense), rep
+    finally:
+        ms.close()
+        ds.close()
