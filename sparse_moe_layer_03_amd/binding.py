@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+# MOE_MI355X_LIB names another build of the same library (the host-only
+# sanitizer build that the host tests load); by default the in-tree one.
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(PKG, "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP",

@@ -31,28 +31,44 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Checking build for host-side tests: AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code only (argument checks,
+# planning, launch set-up; each flag behind -Xarch_host, the device code is
+# built as usual).  The sanitizer runtime is resolved when the library is
+# loaded (LD_PRELOAD of the runtime), so the link line needs no flag.
+SANITIZE_FLAGS = ["-O1", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
+    obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+    flags = [f for f in CFLAGS if not (extra and f == "-O3")]
+    cmd = [HIPCC, *flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stdout}\n{p.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize_out: str = "") -> str:
+    """Builds the library in-tree; with sanitize_out, builds the host-side
+    sanitizer build to that path instead."""
+    obj_dir = os.path.join(os.path.dirname(sanitize_out), "_obj") if sanitize_out else OBJ
+    extra = SANITIZE_FLAGS if sanitize_out else ()
+    lib = sanitize_out or LIB
+    os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    p = subprocess.run(cmd, capture_output=True, text=True)
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    link = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"]
+    p = subprocess.run([*link, *objs, "-o", tmp], capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stdout}\n{p.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
