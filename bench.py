@@ -98,6 +98,13 @@ def parse():
                          "domain (moe_eplb_plan) and report each batch's device max/mean load: "
                          "one expert per slot, the plan of the same batch, and the plan of the "
                          "previous batch applied to it")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="chain this many resident layers (distinct weights, layer i's output "
+                         "is layer i+1's input) and time the chain as one graph, against the "
+                         "same layers timed one at a time; with --prefetch, the next layer's "
+                         "router matrix is read on a second stream while a layer's expert "
+                         "GEMMs run (Infinity Cache warm-up)")
+    ap.add_argument("--prefetch", action="store_true")
     ap.add_argument("--balance", type=float, default=0.0,
                     help="per-expert load-balancing step (moe_balance_update) after the PID; "
                          "0 = off")
@@ -715,6 +722,121 @@ def run_workload(w, args, mdl, dev, cpu=True):
     return line
 
 
+def chain_main(args):
+    """Several resident MoE layers back to back (decode or prefill shape):
+    each layer's output is the next layer's input.  Times (a) every layer
+    alone, each captured as its own graph, and (b) the chain captured as
+    one graph, optionally with the next layer's router matrix read into the
+    cache hierarchy on a side stream while the current layer's expert GEMMs
+    run.  value = tokens/s of the chain (one step = all layers)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from sparse_moe_layer_03_amd import binding as B
+    from sparse_moe_layer_03_amd import synth as S
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    base = S.WORKLOADS[args.workload]
+    L = args.layers
+    ws = [dataclasses.replace(base, seed=base.seed + 101 * i) for i in range(L)]
+    print(f"bench.py: {L} layers of {base.name}, "
+          f"{L * base.expert_weight_bytes() / 1e9:.0f} GB of expert weights", file=sys.stderr,
+          flush=True)
+    mdls = [build_model(w, dev) for w in ws]
+    shape = B.make_shape(base.T, base.d_model, base.n_ffn, base.n_zero, base.d_ff, base.top_k,
+                         base.dtype, base.routed_scaling)
+    bufs = [B.LayerBuffers(shape, dev) for _ in range(L)]
+    x0 = S.make_x(base, 0, dev)
+    side = torch.cuda.Stream()  # default priority
+    sink = torch.empty_like(mdls[0]["wr"])
+    evs = [torch.cuda.Event() for _ in range(L)]
+
+    def layer(i, x, prefetch):
+        m, buf = mdls[i], bufs[i]
+        B.moe_route(shape, x, m["wr"], m["lb"], m["bias0"], buf.topk_idx, buf.topk_gate, None,
+                    buf.ws)
+        B.moe_dispatch(shape, buf.topk_idx, x, buf.counts, buf.offsets, buf.perm, buf.inv_perm,
+                       None, buf.ws)
+        cur = torch.cuda.current_stream()
+        if prefetch and i + 1 < L:
+            evs[i].record(cur)
+            side.wait_event(evs[i])
+            with torch.cuda.stream(side):
+                # read the next router matrix (a plain copy: no reduction, no
+                # memset in the graph) while this layer's GEMMs stream weights
+                sink.copy_(mdls[i + 1]["wr"])
+        B.moe_ffn_gate_up(shape, x, None, buf.perm, buf.offsets, m["wg"], m["wu"], buf.ws)
+        B.moe_ffn_down(shape, buf.offsets, m["wd"], buf.y_perm, buf.ws)
+        B.moe_combine(shape, x, buf.y_perm, buf.topk_idx, buf.topk_gate, buf.inv_perm, buf.y)
+        if prefetch and i + 1 < L:
+            cur.wait_stream(side)
+        return buf.y
+
+    def chain(prefetch):
+        x = x0
+        for i in range(L):
+            x = layer(i, x, prefetch)
+        return x
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+            fn()
+        return g
+
+    def timed(g, reps):
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    # reference outputs (eager chain) for the bitwise check of every variant
+    y_ref = chain(False).clone()
+    torch.cuda.synchronize()
+    singles = [capture(lambda i=i: layer(i, x0 if i == 0 else bufs[i - 1].y, False))
+               for i in range(L)]
+    g_chain = capture(lambda: chain(False))
+    g_pref = capture(lambda: chain(True)) if args.prefetch else None
+    res = {"layers_one_at_a_time_ms": [], "chain_ms": [], "chain_prefetch_ms": []}
+    for _ in range(3):
+        res["layers_one_at_a_time_ms"].append(sum(timed(g, args.steps) for g in singles))
+        res["chain_ms"].append(timed(g_chain, args.steps))
+        if g_pref is not None:
+            res["chain_prefetch_ms"].append(timed(g_pref, args.steps))
+    g_chain.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(bufs[L - 1].y, y_ref))
+    if g_pref is not None:
+        g_pref.replay()
+        torch.cuda.synchronize()
+        same = same and bool(torch.equal(bufs[L - 1].y, y_ref))
+    best = {k: (float(np.min(v)) if v else None) for k, v in res.items()}
+    ms = best["chain_prefetch_ms"] if g_pref is not None else best["chain_ms"]
+    line = {"metric": METRIC + f" ({L} chained layers)", "value": base.T / (ms * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": base.dtype,
+            "data": "synthetic (seeded N(0,1) inputs, N(0,1/d_in) weights, distinct per layer)",
+            "config": {"workload": f"{base.name}x{L}", "T": base.T, "d_model": base.d_model,
+                       "n_ffn": base.n_ffn, "n_zero": base.n_zero, "d_ff": base.d_ff,
+                       "top_k": base.top_k, "layers": L, "prefetch": bool(args.prefetch)},
+            "chain": {**best, "rounds": res, "outputs_equal_eager_chain": same,
+                      "per_layer_ms_chain": best["chain_ms"] / L,
+                      "per_layer_ms_alone": best["layers_one_at_a_time_ms"] / L}}
+    print(json.dumps(line), flush=True)
+    if not same:
+        sys.exit(1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -725,6 +847,10 @@ def main():
         if args.workload == "headline":
             args.workload = "decode_bf16"
         return scmoe_main(args)
+    if args.layers:
+        if args.workload == "headline":
+            args.workload = "decode_bf16"
+        return chain_main(args)
 
     import torch
 
