@@ -137,7 +137,7 @@ def gate_up_kernel_name(w):
         return "grouped_gemm_big_kernel<1,4> (256x256 tiles, gate/up + SwiGLU)"
     if tall:
         return "grouped_gemm_kernel mode 1 (128x128 tiles, gate/up + SwiGLU)"
-    return "grouped_gemm_kernel mode 1 (16x128 tiles, gate/up + SwiGLU)"
+    return "grouped_gemm_kernel mode 1 (16x256 tiles, gate/up + SwiGLU)"
 
 
 def measured_traffic(workload):
@@ -639,8 +639,8 @@ def run_workload(w, args, mdl, dev, cpu=True):
     by_d = [el * (1.0 * u * w.d_model * w.d_ff + a * w.d_ff + a * w.d_model)
             for a, u in zip(A, U)]
     roof_d = kernel_roofline(gate_up_kernel_name(w).replace("<1,", "<2,")
-                             .replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2"),
-                             fl_d, by_d, dn_ms / 1e3, peak_fl)
+                             .replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2")
+                             .replace("16x256", "16x128"), fl_d, by_d, dn_ms / 1e3, peak_fl)
 
     # whole-layer figures per step from its exact A (FFN assignments) and U
     # (touched FFN experts): F = 2 T d E + 6 A d d_ff flops; B_min = the

@@ -372,6 +372,13 @@ static int launch_cfg(const GemmArgs& g, hipStream_t st) {
 #ifndef MOE_SMALL_TILE
 #define MOE_SMALL_TILE 16, 128, 1, 4
 #endif
+// Gate/up streams 256 weight rows (128 gate + 128 up) per few-row tile: half
+// the tiles, each token-row chunk loaded once per 256 weight rows; two
+// workgroups per CU.  Decode gate/up 3.34-3.37 -> 3.21 ms (whole step 5.13-5.17
+// -> 4.99-5.00 ms); down and the router are no faster with it.
+#ifndef MOE_SMALL_TILE_GATE_UP
+#define MOE_SMALL_TILE_GATE_UP 16, 256, 1, 4
+#endif
 
 template <typename T>
 static int launch_typed(int mode, int big, const GemmArgs& g, hipStream_t st) {
@@ -384,7 +391,7 @@ static int launch_typed(int mode, int big, const GemmArgs& g, hipStream_t st) {
   }
   switch (mode) {
     case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, MOE_SMALL_TILE>(g, st);
-    case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, MOE_SMALL_TILE>(g, st);
+    case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, MOE_SMALL_TILE_GATE_UP>(g, st);
     default: return launch_cfg<T, MODE_DOWN, MOE_SMALL_TILE>(g, st);
   }
 }
