@@ -379,6 +379,9 @@ static int launch_cfg(const GemmArgs& g, hipStream_t st) {
 #ifndef MOE_SMALL_TILE_GATE_UP
 #define MOE_SMALL_TILE_GATE_UP 16, 256, 1, 4
 #endif
+#ifndef MOE_SMALL_TILE_DOWN
+#define MOE_SMALL_TILE_DOWN MOE_SMALL_TILE
+#endif
 
 template <typename T>
 static int launch_typed(int mode, int big, const GemmArgs& g, hipStream_t st) {
@@ -392,7 +395,7 @@ static int launch_typed(int mode, int big, const GemmArgs& g, hipStream_t st) {
   switch (mode) {
     case MODE_ROUTER: return launch_cfg<T, MODE_ROUTER, MOE_SMALL_TILE>(g, st);
     case MODE_GATE_UP: return launch_cfg<T, MODE_GATE_UP, MOE_SMALL_TILE_GATE_UP>(g, st);
-    default: return launch_cfg<T, MODE_DOWN, MOE_SMALL_TILE>(g, st);
+    default: return launch_cfg<T, MODE_DOWN, MOE_SMALL_TILE_DOWN>(g, st);
   }
 }
 
