@@ -105,6 +105,18 @@ def test_topk_every_selected_beats_unselected_and_ascending():
     np.testing.assert_array_equal(m, s[:, 8] - s[:, 9])
 
 
+def test_topk_margin_hand_values():
+    # keys chosen so every gap is a short dyadic fraction: the k-th minus the
+    # (k+1)-th largest key, written out by hand; ties give a zero margin and
+    # k = E has no (k+1)-th key
+    keys = np.array([[0.25, 0.75, 0.5, 0.125],
+                     [0.5, 0.5, 0.25, 0.0]])
+    np.testing.assert_array_equal(O.topk_margin(keys, 1), [0.25, 0.0])
+    np.testing.assert_array_equal(O.topk_margin(keys, 2), [0.25, 0.25])
+    np.testing.assert_array_equal(O.topk_margin(keys, 3), [0.125, 0.25])
+    assert np.isinf(O.topk_margin(keys, 4)).all()
+
+
 def test_zero_bias_selection_equals_logit_topk():
     # softmax is monotone: with zero correction bias the chosen set is the
     # top-k of the raw logits (pins that the bias is added to the score only)
