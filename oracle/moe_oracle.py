@@ -86,6 +86,7 @@ __all__ = [
     "pid_update",
     "pid_update_f32",
     "balance_update",
+    "balance_update_f32",
     "eplb_replicas",
     "eplb_slots",
     "eplb_place",
@@ -361,6 +362,25 @@ def balance_update(counts, n_ffn, bias, gamma):
     delta = float(gamma) * (s - s.mean())
     new_bias = _f64(bias).copy()
     new_bias[:n_ffn] += delta
+    return new_bias
+
+
+def balance_update_f32(counts, n_ffn, bias, gamma):
+    """``balance_update`` in float32, as the layer defines the step: with
+    A = sum_{e<N} counts[e], s_e = sign(A - N counts[e]) and S = sum s_e
+    (exact integers), every FFN expert's bias becomes
+        bias[e] + f32(gamma) * (f32(N s_e - S) / f32(N)),
+    one rounding for the quotient, one for the product, one for the sum.
+    ``bias`` is returned as float32."""
+    f = np.float32
+    c = np.asarray(counts, dtype=np.int64)[:n_ffn]
+    a = int(c.sum())
+    s = np.sign(a - n_ffn * c).astype(np.int64)
+    S = int(s.sum())
+    frac = (n_ffn * s - S).astype(np.float32) / f(n_ffn)
+    step = f(gamma) * frac
+    new_bias = np.asarray(bias, dtype=np.float32).copy()
+    new_bias[:n_ffn] = new_bias[:n_ffn] + step
     return new_bias
 
 

@@ -1,5 +1,6 @@
-"""GPU per-expert load balancing: the bias step equals the oracle's on the
-same counts, and on the skewed workload it narrows the FFN load gap."""
+"""GPU per-expert load balancing: the bias step equals, bit for bit, the
+oracle's float32 step on the same counts (and lies within its rounding of
+the float64 one), and on the skewed workload it narrows the FFN load gap."""
 
 import json
 import os
@@ -29,8 +30,12 @@ def test_balance_step_matches_oracle(N, Z, seed):
     for gamma in (0.0, 0.01, 0.37):
         B.moe_balance_update(s, gamma, cd, bd)
         bias_ref = O.balance_update(counts, N, bias.astype(np.float64), gamma)
+        bias_32 = O.balance_update_f32(counts, N, bias, gamma)
         torch.cuda.synchronize()
         got = bd.cpu().numpy()
+        # bit for bit against the float32 step, and within its rounding of
+        # the float64 one
+        np.testing.assert_array_equal(got.view(np.int32), bias_32.view(np.int32))
         np.testing.assert_allclose(got, bias_ref, rtol=0, atol=4e-7 * max(1.0, gamma * 4))
         np.testing.assert_array_equal(got[N:], bias[N:])
         bias = got.copy()
@@ -45,7 +50,8 @@ def test_skewed_workload_balancing_narrows_load_gap():
     params = B.MoePidParams(*w.pid)
     gamma = 0.01
     bias_o = m.bias.cpu().numpy().astype(np.float64)
-    st = O.PidState()
+    bias_32 = m.bias.cpu().numpy().astype(np.float32)
+    st, st32 = O.PidState(), O.PidState()
     ratios = []
     for b in range(40):
         x = S.make_x(w, b, "cuda")
@@ -55,7 +61,11 @@ def test_skewed_workload_balancing_narrows_load_gap():
         c = buf.counts.cpu().numpy()
         bias_o, st, _ = O.pid_update(c, w.n_ffn, w.T, bias_o, st, *w.pid)
         bias_o = O.balance_update(c, w.n_ffn, bias_o, gamma)
-        np.testing.assert_allclose(m.bias.cpu().numpy(), bias_o, rtol=2e-6, atol=2e-6)
+        bias_32, st32, _ = O.pid_update_f32(c, w.n_ffn, w.T, bias_32, st32, *w.pid)
+        bias_32 = O.balance_update_f32(c, w.n_ffn, bias_32, gamma)
+        g_bias = m.bias.cpu().numpy()
+        np.testing.assert_array_equal(g_bias.view(np.int32), bias_32.view(np.int32))
+        np.testing.assert_allclose(g_bias, bias_o, rtol=2e-6, atol=2e-6)
         cf = c[: w.n_ffn]
         ratios.append(cf.max() / max(cf.mean(), 1e-9))
     say(f"  max/mean FFN load: batch 0 {ratios[0]:.1f}, min over 20-40 {min(ratios[20:]):.1f}")

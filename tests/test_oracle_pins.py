@@ -557,3 +557,21 @@ def test_eplb_plan_leaves_routing_alone_and_narrows_the_device_gap():
     assert p["device_load"].max() / p["device_load"].mean() < 0.5 * naive.max() / naive.mean()
     np.testing.assert_array_equal(
         O.eplb_device_loads(c, p["replicas"], p["slot_device"], 8), p["device_load"])
+
+
+def test_balance_f32_on_dyadic_values_and_against_the_float64_step():
+    # N = 4 and gamma = 0.5: every quotient and product is dyadic, so the
+    # float32 step lands exactly on the hand values; counts 1, 2, 3, 10 ->
+    # mean 4, signs +1 +1 +1 -1, S = 2, steps 0.5 * (4 s - 2) / 4
+    b = O.balance_update_f32(np.array([1, 2, 3, 10, 99]), 4, np.zeros(5, np.float32), 0.5)
+    assert b.dtype == np.float32
+    assert b.tolist() == [0.25, 0.25, 0.25, -0.75, 0.0]
+    r_ = rng(90)
+    for _ in range(50):
+        N = int(r_.integers(1, 300))
+        c = r_.integers(0, 1000, N + 3)
+        bias = r_.normal(0, 0.1, N + 3).astype(np.float32)
+        g = float(r_.uniform(0, 0.05))
+        b32 = O.balance_update_f32(c, N, bias, g)
+        b64 = O.balance_update(c, N, bias.astype(np.float64), g)
+        np.testing.assert_allclose(b32, b64, rtol=0, atol=2e-7)
