@@ -121,6 +121,15 @@ def gate_up_units(w, A, U):
     return flops, byts
 
 
+def down_kernel_name(w):
+    """The down GEMM's kernel for this shape (256x256 tiles only)."""
+    name = gate_up_kernel_name(w)
+    if name.startswith("grouped_gemm_big_kernel"):
+        return "grouped_gemm_big_kernel<2,4> (256x256 tiles, down)"
+    return (name.replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2")
+            .replace("16x256", "16x128"))
+
+
 def gate_up_kernel_name(w):
     """Which gate/up kernel the library launches for this shape (the same
     tests the library makes: at least 32 assignments per expert and at least
@@ -134,7 +143,9 @@ def gate_up_kernel_name(w):
             or Tk // w.n_ffn >= 64)
     if (tall and w.dtype == "bf16" and w.d_model % 128 == 0 and w.d_ff % 128 == 0
             and cdiv(Tk, 256) * min(w.d_ff // 128, w.d_model // 256) >= 64):
-        return "grouped_gemm_big_kernel<1,4> (256x256 tiles, gate/up + SwiGLU)"
+        return ("grouped_gemm_big_kernel<1,4,*> (320x192 tiles for the experts of 257..320 rows "
+                "when they fill 4 rounds of the grid, then 256x256 tiles for the rest; "
+                "gate/up + SwiGLU; event time of both launches)")
     if tall:
         return "grouped_gemm_kernel mode 1 (128x128 tiles, gate/up + SwiGLU)"
     return "grouped_gemm_kernel mode 1 (16x256 tiles, gate/up + SwiGLU)"
@@ -638,9 +649,7 @@ def run_workload(w, args, mdl, dev, cpu=True):
     fl_d = [2.0 * a * w.d_model * w.d_ff for a in A]
     by_d = [el * (1.0 * u * w.d_model * w.d_ff + a * w.d_ff + a * w.d_model)
             for a, u in zip(A, U)]
-    roof_d = kernel_roofline(gate_up_kernel_name(w).replace("<1,", "<2,")
-                             .replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2")
-                             .replace("16x256", "16x128"), fl_d, by_d, dn_ms / 1e3, peak_fl)
+    roof_d = kernel_roofline(down_kernel_name(w), fl_d, by_d, dn_ms / 1e3, peak_fl)
 
     # whole-layer figures per step from its exact A (FFN assignments) and U
     # (touched FFN experts): F = 2 T d E + 6 A d d_ff flops; B_min = the

@@ -252,6 +252,15 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int
                       (hipStream_t)stream);
 }
 
+// Gate/up experts of 257..320 rows on the 320 x 192 tiles, where the shape
+// allows.
+static void set_r320(const moe_shape* s, GemmArgs& g, hipStream_t st) {
+  if (plan::ffn_use_r320(s->T, s->top_k, s->n_ffn, s->d_ff, big_grid(st))) {
+    g.r320_lo = plan::kR320Lo;
+    g.r320_hi = plan::kR320Hi;
+  }
+}
+
 int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const int32_t* perm,
                     const int32_t* offsets, const void* w_gate, const void* w_up, void* ws,
                     void* stream) {
@@ -274,8 +283,10 @@ int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const
   g.ngroups = s->n_ffn;
   g.top_k = s->top_k;
   g.ksplit = 1;
-  if (ffn_use_big(s, x_perm == nullptr, (hipStream_t)stream))
+  if (ffn_use_big(s, x_perm == nullptr, (hipStream_t)stream)) {
+    set_r320(s, g, (hipStream_t)stream);
     return launch_gemm_big(1, g, (hipStream_t)stream);
+  }
   return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 

@@ -29,6 +29,12 @@
 //    not all after the barrier: their issue stalls until earlier ones have
 //    drained into LDS, and eight waves issuing at once had kept every SIMD's
 //    MFMAs waiting for about a third of each step.
+//  * A second tile shape for gate/up, 320 x 192 on 16x16x32 MFMAs, takes the
+//    experts of 257..320 rows in one tile (a batch averaging 256 rows per
+//    expert has about half of them there); split into two 256-row tiles,
+//    each would stream the expert's whole weight slice through LDS.  Its own
+//    launch runs before the 256-row one, when those experts fill four rounds
+//    of the grid.
 //  * Balanced tile heights: an expert with m rows gets ceil(m / 256) tiles of
 //    equal height (a multiple of 32).  A wave runs the MFMAs of only the
 //    32-row blocks that hold rows: the K loop exists once per count of
@@ -73,22 +79,50 @@ constexpr int kBigDescRegs = 4;  // tile descriptors: 64 per register
 static_assert(64 * kBigDescRegs == plan::kBigMaxTilesPerWg, "host bound on items per workgroup");
 static_assert(kBigMaxGroups == plan::kBigMaxGroups && kBigTileRows == plan::kBigTileRows,
               "host plan matches the kernel");
+static_assert(plan::kR320Lo > kBigTileRows && plan::kR320Hi <= 320, "320-row tiles");
 
-template <int MODE, int MG>
+// The two tile shapes.  256 x 256 on 32x32x16 MFMAs, 8 waves of 128 x 64:
+// every expert except those with 257..320 rows.  320 x 192 on 16x16x32
+// MFMAs, 8 waves of 80 x 96 (120 accumulators per lane, 152 KiB of LDS):
+// an expert with 257..320 rows in one tile instead of two, so its weight
+// slice passes through LDS once.
+template <bool R320>
+struct BigShape {
+  static constexpr int BM = R320 ? 320 : 256, BN = R320 ? 192 : 256;
+  static constexpr int WM = R320 ? 4 : 2, WN = R320 ? 2 : 4;
+  static constexpr int BLK = R320 ? 16 : 32;  // rows and weight rows per MFMA block
+  static constexpr int KSL = R320 ? 32 : 16;  // K per MFMA
+};
+
+// Whether a group of `cnt` rows runs on the 320-row kernel (both kernels
+// decide alike, so every group runs on exactly one of them).
+__device__ __forceinline__ bool rows320(const GemmArgs& g, int cnt) {
+  return g.r320_hi > 0 && cnt >= g.r320_lo && cnt <= g.r320_hi && cnt <= 320;
+}
+
+template <int MODE, int MG, bool R320>
 __global__ void __launch_bounds__(512, 1)
 grouped_gemm_big_kernel(GemmArgs g) {
-  constexpr int BM = kBigTileRows, BN = 256, WM = 2, WN = 4, NW = WM * WN, NT = 64 * NW;
+  using SH = BigShape<R320>;
+  constexpr int BM = SH::BM, BN = SH::BN, WM = SH::WM, WN = SH::WN, NW = WM * WN, NT = 64 * NW;
+  constexpr int BLK = SH::BLK;
   constexpr int RB = 128;                           // bytes per stage row
   constexpr int RPK = 1024 / RB;                    // stage rows per KiB
   constexpr int KS = RB / 2;                        // K elements per stage
   constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int MB = WTM / 32, NB = WTN / 32;       // 32x32 blocks per wave
+  constexpr int MB = WTM / BLK, NB = WTN / BLK;     // MFMA blocks per wave
   constexpr int HN = (MODE == 1) ? BN / 2 : BN;     // output columns per tile
   constexpr int A_PW = BM / RPK / NW;               // DMA instructions per wave
   constexpr int B_PW = BN / RPK / NW;
-  constexpr int NKK = KS / 16;                      // MFMA K-slices per stage
+  constexpr int NKK = KS / SH::KSL;                 // MFMA K-slices per stage
+  constexpr int DPS = (A_PW + B_PW) / NKK;          // DMA instructions per slice
+  using acc_t = std::conditional_t<R320, f32x4_t, f32x16_t>;
   static_assert(MODE != 1 || NB % 2 == 0, "gate/up pairing");
   static_assert(A_PW + 2 * B_PW < 64, "vmcnt range");
+  static_assert(DPS * NKK == A_PW + B_PW, "DMA spread evenly over the slices");
+  static_assert(!R320 || MODE == 1, "320-row tiles: gate/up only");
+  static_assert(HN % RPK == 0, "one DMA instruction's rows lie in one gate/up half");
+  static_assert(BM * RB * 2 + BN * RB * 3 <= 160 * 1024, "LDS");
 
   // One array per stage (see the header comment).
   __shared__ __attribute__((aligned(1024))) char s_a0[BM * RB];
@@ -101,7 +135,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
-  const int r32 = lane & 31, kg = lane >> 5;
+  const int rin = lane & (BLK - 1);  // row of an MFMA block this lane supplies
+  const int kg = lane / BLK;         // its 16-byte K chunk within the K-slice
 
   const int ngroups = g.ngroups;
   const int ntiles = (g.N + HN - 1) / HN;
@@ -115,9 +150,34 @@ grouped_gemm_big_kernel(GemmArgs g) {
   // guarantees at most 64 * kBigDescRegs tiles per workgroup); the tile loop
   // reads them back with readlane.
   int* s_pref = reinterpret_cast<int*>(s_a0);  // ngroups + 1 <= 1025 ints
-  int* s_scan = reinterpret_cast<int*>(s_a1);  // NT / 64 ints
+  int* s_scan = reinterpret_cast<int*>(s_a1);  // NT / 64 + 1 ints
+  constexpr int PER = (kBigMaxGroups + NT - 1) / NT;
+  // The 320-row tiles are used only when they fill at least four rounds of
+  // the grid (their launch's partly idle last round costs up to one round);
+  // both tile shapes count the groups alike.
+  bool use320 = false;
+  if (MODE == 1 && g.r320_hi > 0) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int gi = tid * PER + i;
+      if (gi < ngroups && rows320(g, g.offsets[gi + 1] - g.offsets[gi])) ++n;
+    }
+    const int incl = block_inclusive_scan<NT>(n, s_scan);
+    if (tid == NT - 1) s_scan[NT / 64] = incl;
+    __syncthreads();
+    constexpr int HN320 = BigShape<true>::BN / 2;
+    use320 = s_scan[NT / 64] * ((g.N + HN320 - 1) / HN320) >= 4 * (int)gridDim.x;
+  }
+  // m-tiles of a group of cnt rows on this kernel (none for the groups the
+  // other tile shape runs)
+  auto mtiles = [&](int cnt) -> int {
+    if (MODE == 0) return (cnt + BM - 1) / BM;
+    const bool r = use320 && rows320(g, cnt);
+    if constexpr (R320) return r ? 1 : 0;
+    else return r ? 0 : (cnt + BM - 1) / BM;
+  };
   {
-    constexpr int PER = (kBigMaxGroups + NT - 1) / NT;
     int loc[PER];
     int run = 0;
 #pragma unroll
@@ -125,7 +185,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       const int gi = tid * PER + i;
       int mt = 0;
       if (gi < ngroups)
-        mt = ((MODE == 0 ? g.M : g.offsets[gi + 1] - g.offsets[gi]) + BM - 1) / BM;
+        mt = mtiles(MODE == 0 ? g.M : g.offsets[gi + 1] - g.offsets[gi]);
       run += mt;
       loc[i] = run;
     }
@@ -191,7 +251,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int grp = (MODE == 0) ? 0 : (int)(d & 1023u);
     const int tp0 = (MODE == 0) ? 0 : (int)(d >> 10);
     const int cnt_g = (MODE == 0) ? g.M : g.offsets[grp + 1] - g.offsets[grp];
-    const int mt_g = (cnt_g + BM - 1) / BM;
+    const int mt_g = mtiles(cnt_g);
     const int local = t - tp0 * ntiles;
     // Within an expert, tiles go in groups of MG m-tiles x all n-tiles (n-tile
     // major inside a group), so the tiles that run together on one XCD share
@@ -215,8 +275,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
       if (m0 >= m_end) continue;
     }
     const int n0 = nt * HN;
-    // 32-row blocks of this wave that hold rows: i with (i*WM + wm)*32 < rows
-    const int nrb = (m_end - m0 + 31) / 32;
+    // row blocks of this wave that hold rows: i with (i*WM + wm)*BLK < rows
+    const int nrb = (m_end - m0 + BLK - 1) / BLK;
     const int mba = min(MB, (nrb - wm + WM - 1) / WM);
 
     // ---- per-lane DMA source offsets (32-bit; bases are wave-uniform, and
@@ -245,20 +305,26 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const char* b_base0 = (const char*)g.b0 + (size_t)grp * g.N * row_bytes;
     const char* b_base1 =
         (MODE == 1) ? (const char*)g.b1 + (size_t)grp * g.N * row_bytes : b_base0;
+    // gate rows fill the first half of a gate/up weight tile, up rows the
+    // second; the 8 rows one DMA instruction fills lie in one half (with 256
+    // rows the half is fixed per q, with 192 it depends on the wave)
+    auto up_half = [&](int q) {
+      return MODE == 1 && (R320 ? (wave + q * NW) * RPK >= HN : (q * NW) * RPK >= HN);
+    };
     uint32_t b_off[B_PW];
 #pragma unroll
     for (int q = 0; q < B_PW; ++q) {
       const int r = (wave + q * NW) * RPK + dma_row;
-      int n = (MODE == 1 && r >= HN) ? n0 + r - HN : n0 + r;
+      int n = up_half(q) ? n0 + r - HN : n0 + r;
       if (n > g.N - 1) n = g.N - 1;
       b_off[q] = (uint32_t)(n * row_bytes) + k_base + swz(r, dma_slot) * 16;
     }
 
-    f32x16_t acc[MB][NB];
+    acc_t acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < NB; ++j) acc[i][j] = acc_t{};
 
     auto stage_a = [&](auto sc) -> char* {
       constexpr int S = decltype(sc)::value;
@@ -285,20 +351,17 @@ grouped_gemm_big_kernel(GemmArgs g) {
       const size_t off = (size_t)ks * RB;
 #pragma unroll
       for (int q = 0; q < B_PW; ++q) {
-        // gate rows fill the first half of the B tile, up rows the second
-        // (wave < NW, so the half is fixed per q)
-        const char* bb = (MODE == 1 && (q * NW) * RPK >= HN) ? b_base1 : b_base0;
+        const char* bb = up_half(q) ? b_base1 : b_base0;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
                                          (lds_void_t*)(sb + (wave + q * NW) * 1024), 16, 0, 0);
       }
     };
-    static_assert(MODE != 1 || (HN % (NW * RPK) == 0), "gate/up halves align with q");
 
     auto brow = [&](int j) {
       if (MODE == 1)
-        return (j < NB / 2) ? wn * (WTN / 2) + j * 32 + r32
-                            : HN + wn * (WTN / 2) + (j - NB / 2) * 32 + r32;
-      return wn * WTN + j * 32 + r32;
+        return (j < NB / 2) ? wn * (WTN / 2) + j * BLK + rin
+                            : HN + wn * (WTN / 2) + (j - NB / 2) * BLK + rin;
+      return wn * WTN + j * BLK + rin;
     };
 
     // One K-step of 64 on token-row stage AS and weight stage BS, with MBA
@@ -342,41 +405,92 @@ grouped_gemm_big_kernel(GemmArgs g) {
       }
       // favour this wave's MFMA issue over the other wave on the SIMD
       __builtin_amdgcn_s_setprio(1);
+      // DMA load L of a main-loop step: token rows of step ks+1 for
+      // L < A_PW, then weights of step ks+2; slice kk issues loads
+      // kk*DPS .. kk*DPS + DPS-1, so token rows always go first
+      auto dma_one = [&](int L) {
+        if (L < A_PW) {
+          char* sa2 = stage_a(std::integral_constant<int, (AS + 1) % 2>{});
+          const size_t off = (size_t)(R320 ? min(ks + 1, nK - 1) : ks + 1) * RB;
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[L] + off),
+                                           (lds_void_t*)(sa2 + (wave + L * NW) * 1024), 16, 0, 0);
+        } else {
+          const int q = L - A_PW;
+          char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
+          const size_t off = (size_t)(R320 ? min(ks + 2, nK - 1) : ks + 2) * RB;
+          const char* bb = up_half(q) ? b_base1 : b_base0;
+          __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
+                                           (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, 0);
+        }
+      };
+      auto dma_piece = [&](int kk) {
+#pragma unroll
+        for (int L = kk * DPS; L < kk * DPS + DPS; ++L) dma_one(L);
+      };
+      auto frag = [&](const char* base, int r, int c) {
+        return *reinterpret_cast<const u32x4_t*>(&base[r * RB + (swz(r, c) << 4)]);
+      };
+      if constexpr (R320) {
+        // Two K-slices of 32 per stage.  Slice 0's fragments are read after
+        // the barrier; slice 1's under slice 0's MFMAs, which run token-row
+        // block by block (i-major): each token-row fragment of slice 1 once
+        // slice 0's last MFMA on that block has issued, the weight fragments
+        // one by one in the last block, so each can take the registers of
+        // the fragment it replaces (120 accumulators leave no room for a
+        // second fragment set).  A scheduling fence closes every block's
+        // group; the slice's DMA loads are spread over the groups.
+        u32x4_t a0[MBA], a1[MBA], w0[NB], w1[NB];
+#pragma unroll
+        for (int i = 0; i < MBA; ++i) a0[i] = frag(sa, (i * WM + wm) * BLK + rin, kg);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) w0[j] = frag(sb, brow(j), kg);
+        __builtin_amdgcn_sched_group_barrier(0x100, MBA + NB, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+          for (int i = 0; i < MBA; ++i) {
+            const int d_lo = (i * DPS + MBA - 1) / MBA, d_hi = ((i + 1) * DPS + MBA - 1) / MBA;
+            if constexpr (SPREAD) {
+#pragma unroll
+              for (int d = d_lo; d < d_hi; ++d) dma_one(kk * DPS + d);
+            }
+            const bool last = kk == 0 && i == MBA - 1;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, kk == 0 ? w0[j] : w1[j]),
+                  __builtin_bit_cast(bf16x8_t, kk == 0 ? a0[i] : a1[i]), acc[i][j], 0, 0, 0);
+              if (last) w1[j] = frag(sb, brow(j), 4 + kg);
+            }
+            if (kk == 0) a1[i] = frag(sa, (i * WM + wm) * BLK + rin, 4 + kg);
+            if constexpr (SPREAD) {
+#pragma unroll
+              for (int d = d_lo; d < d_hi; ++d) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            if (last) {
+#pragma unroll
+              for (int j = 0; j < NB; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              }
+            } else {
+              __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+            }
+            if (kk == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
       u32x4_t af[2][MBA], bfr[2][NB];
       auto load = [&](int set, int kk) {
         const int c = kk * 2 + kg;
 #pragma unroll
-        for (int i = 0; i < MBA; ++i) {
-          const int r = (i * WM + wm) * 32 + r32;
-          af[set][i] = *reinterpret_cast<const u32x4_t*>(&sa[r * RB + (swz(r, c) << 4)]);
-        }
+        for (int i = 0; i < MBA; ++i) af[set][i] = frag(sa, (i * WM + wm) * BLK + rin, c);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int r = brow(j);
-          bfr[set][j] = *reinterpret_cast<const u32x4_t*>(&sb[r * RB + (swz(r, c) << 4)]);
-        }
+        for (int j = 0; j < NB; ++j) bfr[set][j] = frag(sb, brow(j), c);
       };
-      // DMA pieces of slice kk: A loads 2kk, 2kk+1 (kk < 2), B loads 2(kk-2), 2(kk-2)+1
-      auto dma_piece = [&](int kk) {
-        if (kk < 2) {
-          char* sa2 = stage_a(std::integral_constant<int, (AS + 1) % 2>{});
-          const size_t off = (size_t)(ks + 1) * RB;
-#pragma unroll
-          for (int q = 2 * kk; q < 2 * kk + 2; ++q)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
-                                             (lds_void_t*)(sa2 + (wave + q * NW) * 1024), 16, 0, 0);
-        } else {
-          char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
-          const size_t off = (size_t)(ks + 2) * RB;
-#pragma unroll
-          for (int q = 2 * (kk - 2); q < 2 * (kk - 2) + 2; ++q) {
-            const char* bb = (MODE == 1 && (q * NW) * RPK >= HN) ? b_base1 : b_base0;
-            __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
-                                             (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, 0);
-          }
-        }
-      };
-      static_assert(!SPREAD || (A_PW == 4 && B_PW == 4 && NKK == 4), "two DMA loads per slice");
+      static_assert(R320 || !SPREAD || (A_PW == 4 && B_PW == 4 && NKK == 4), "two DMA loads per slice");
       // Pin the schedule (the default one sinks every LDS read next to its
       // first use and stalls on it): the first slice's reads, then each
       // slice's MFMAs with the next slice's reads interleaved 1:1 at the
@@ -424,6 +538,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
         }
         if constexpr (SPREAD) __builtin_amdgcn_sched_barrier(0);
       }
+      }
       __builtin_amdgcn_s_setprio(0);
     };
 
@@ -445,7 +560,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
       issue_b(I0{}, 0);
       issue_b(I1{}, 1);  // nK >= 2
       int ks = 0;
-      for (; ks + 8 <= nK; ks += 6) {
+      // 320-row tiles run every step here, the last ones refilling stages
+      // that are never read (the refill K-step is clamped to the last one)
+      for (; ks + (R320 ? 6 : 8) <= nK; ks += 6) {
         kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
         kstep(mbac, I1{}, I1{}, T{}, T{}, ks + 1);
         kstep(mbac, I0{}, I2{}, T{}, T{}, ks + 2);
@@ -453,19 +570,31 @@ grouped_gemm_big_kernel(GemmArgs g) {
         kstep(mbac, I0{}, I1{}, T{}, T{}, ks + 4);
         kstep(mbac, I1{}, I2{}, T{}, T{}, ks + 5);
       }
+      if constexpr (R320) {
+        // nK is even: 0, 2 or 4 steps remain
+        if (ks + 2 <= nK) {
+          kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
+          kstep(mbac, I1{}, I1{}, T{}, T{}, ks + 1);
+        }
+        if (ks + 4 <= nK) {
+          kstep(mbac, I0{}, I2{}, T{}, T{}, ks + 2);
+          kstep(mbac, I1{}, I0{}, T{}, T{}, ks + 3);
+        }
+      }
       return ks;
     };
     // a wave with no rows (mba == 0) still loads and waits with the others;
     // its one block of clamped rows is never stored
     int ks;
-    if (mba >= 4) ks = kloop(std::integral_constant<int, 4>{});
+    if (R320 && mba >= 5) ks = kloop(std::integral_constant<int, R320 ? 5 : 4>{});
+    else if (mba >= 4) ks = kloop(std::integral_constant<int, 4>{});
     else if (mba == 3) ks = kloop(std::integral_constant<int, 3>{});
     else if (mba == 2) ks = kloop(std::integral_constant<int, 2>{});
     else ks = kloop(std::integral_constant<int, 1>{});
     // The last 2, 4 or 6 steps run every block (one copy of the code; blocks
     // without rows are never stored) with refills decided at run time.
-    {
-      using M4 = std::integral_constant<int, 4>;
+    if constexpr (!R320) {
+      using M4 = std::integral_constant<int, MB>;
       kstep(M4{}, I0{}, I0{}, ks + 1 < nK, ks + 2 < nK, ks);
       kstep(M4{}, I1{}, I1{}, ks + 2 < nK, ks + 3 < nK, ks + 1);
       if (ks + 4 <= nK) {
@@ -479,12 +608,46 @@ grouped_gemm_big_kernel(GemmArgs g) {
     }
 
     // ---- epilogue.  Weights were the MFMA row operand, so block (i, j) is
-    // C^T: lane (r32, kg) holds, for quad q = v / 4, the 4 consecutive output
-    // columns 8q + 4kg + {0..3} of token row r32 -> one packed 8-byte store.
-    // Blocks past the wave's active ones hold rows >= m_end and are skipped.
+    // C^T.  32x32 blocks: lane (r32, kg) holds, for quad q = v / 4, the 4
+    // consecutive output columns 8q + 4kg + {0..3} of token row r32.  16x16
+    // blocks: lane (r16, kg) holds columns 4kg + {0..3} of token row r16.
+    // Either way one packed 8-byte store per 4 columns.  Blocks past the
+    // wave's active ones hold rows >= m_end and are skipped.
+    auto bf16x4 = [](float v0, float v1, float v2, float v3) {
+      const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v0) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v1) << 16);
+      const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v2) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v3) << 16);
+      return make_uint2(lo, hi);
+    };
+    // silu(z) = z * sigmoid(z) with hardware exp2 / reciprocal (H is
+    // rounded to bf16 right after)
+    auto swiglu = [](float z, float u) {
+      const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504f));
+      return z * sg * u;
+    };
+    if constexpr (R320) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int r = m0 + (i * WM + wm) * BLK + rin;
+        if (r < m_end) {
+          char* crow = (char*)g.c + (size_t)(row0 + r) * g.N * 2;
+#pragma unroll
+          for (int j = 0; j < NB / 2; ++j) {
+            const int col = n0 + wn * (WTN / 2) + j * BLK + 4 * kg;
+            const acc_t& z = acc[i][j];
+            const acc_t& u = acc[i][j + NB / 2];
+            if (col + 3 < g.N)
+              *reinterpret_cast<uint2*>(crow + col * 2) =
+                  bf16x4(swiglu(z[0], u[0]), swiglu(z[1], u[1]), swiglu(z[2], u[2]),
+                         swiglu(z[3], u[3]));
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int r = m0 + (i * WM + wm) * 32 + r32;
+      const int r = m0 + (i * WM + wm) * 32 + rin;
       if (r < m_end) {
         char* crow = (char*)g.c + (size_t)(row0 + r) * g.N * 2;
         float* prow = (float*)g.c + ((size_t)tsplit * g.M + r) * g.N;  // mode 0
@@ -511,36 +674,23 @@ grouped_gemm_big_kernel(GemmArgs g) {
               const int col = n0 + wn * (WTN / 2) + j * 32 + 8 * q + 4 * kg;
               float hv[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float z = acc[i][j][4 * q + e];
-                // silu(z) = z * sigmoid(z) with hardware exp2 / reciprocal
-                // (H is rounded to bf16 right after)
-                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504f));
-                hv[e] = z * sg * acc[i][j + NB / 2][4 * q + e];
-              }
-              if (col + 3 < g.N) {
-                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[0]) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[1]) << 16);
-                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[2]) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hv[3]) << 16);
-                *reinterpret_cast<uint2*>(crow + col * 2) = make_uint2(lo, hi);
-              }
+              for (int e = 0; e < 4; ++e) hv[e] = swiglu(acc[i][j][4 * q + e], acc[i][j + NB / 2][4 * q + e]);
+              if (col + 3 < g.N)
+                *reinterpret_cast<uint2*>(crow + col * 2) = bf16x4(hv[0], hv[1], hv[2], hv[3]);
             }
           } else {
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
               const int col = n0 + wn * WTN + j * 32 + 8 * q + 4 * kg;
-              if (col + 3 < g.N) {
-                const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q]) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q + 1]) << 16);
-                const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q + 2]) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q + 3]) << 16);
-                *reinterpret_cast<uint2*>(crow + col * 2) = make_uint2(lo, hi);
-              }
+              if (col + 3 < g.N)
+                *reinterpret_cast<uint2*>(crow + col * 2) =
+                    bf16x4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                           acc[i][j][4 * q + 3]);
             }
           }
         }
       }
+    }
     }
   }
 }
@@ -555,12 +705,24 @@ int big_grid(hipStream_t st) {
   return grid < 8 ? 8 : grid;
 }
 
-template <int MODE>
+template <int MODE, bool R320>
 static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
-  auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG>;
+  auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG, R320>;
   if (device_cu_count() <= 0) return MOE_EHIP;
   hipLaunchKernelGGL(kern, dim3(big_grid(st)), dim3(512), 0, st, g);
   return check_launch();
+}
+
+// Expert modes: gate/up runs the groups of r320_lo..r320_hi rows on
+// 320 x 192 tiles and the others on 256 x 256 tiles (two launches on the
+// same stream; they write disjoint rows).
+template <int MODE>
+static int launch_big_expert(const GemmArgs& g, hipStream_t st) {
+  if (MODE == 1 && g.r320_hi > 0) {
+    const int rc = launch_big_mode<1, true>(g, st);
+    if (rc != MOE_OK) return rc;
+  }
+  return launch_big_mode<MODE, false>(g, st);
 }
 
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
@@ -568,9 +730,10 @@ int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
   if (mode == 0) {
     // each split covers an even number (>= 2) of 64-wide K-steps
     if (g.ngroups != 1 || g.ksplit < 1 || (g.K / 64) % (2 * g.ksplit) != 0) return MOE_EINVAL;
-    return launch_big_mode<0>(g, st);
+    return launch_big_mode<0, false>(g, st);
   }
-  return mode == 1 ? launch_big_mode<1>(g, st) : launch_big_mode<2>(g, st);
+  if (g.r320_hi > 0 && (mode != 1 || g.r320_lo < 1 || g.r320_hi > 320)) return MOE_EINVAL;
+  return mode == 1 ? launch_big_expert<1>(g, st) : launch_big_expert<2>(g, st);
 }
 
 }  // namespace moe

@@ -37,6 +37,12 @@ inline long big_ntiles(int mode, long d_model, long d_ff) {
   return mode == 1 ? cdiv(d_ff, kBigGateUpCols) : cdiv(d_model, kBigDownCols);
 }
 
+// In gate/up, experts with 257..320 rows run on a second tile shape,
+// 320 x 192 (96 H columns per tile), one tile each instead of two 256-row
+// tiles that would each stream the weight slice.
+constexpr int kR320Lo = 257, kR320Hi = 320;
+inline long big320_ntiles(long d_ff) { return cdiv(d_ff, 96); }
+
 // Upper bound on the work items one workgroup of a G-workgroup grid runs.
 // The kernel's items are the tiles, except that a last round at most half
 // full has its tiles cut into f <= G / rem row slices; then the items are
@@ -78,6 +84,16 @@ inline bool ffn_use_big(long T, long top_k, long n_ffn, long n_zero, long d_mode
   if (mt >= kBigMaxMTiles) return false;
   const long nt = std::max(big_ntiles(1, d_model, d_ff), big_ntiles(2, d_model, d_ff));
   return big_items_per_wg_max(mt * nt, G) <= kBigMaxTilesPerWg;
+}
+
+// Whether a many-row gate/up also uses the 320-row tiles: at most
+// min(n_ffn, T*k / 257) groups take one such tile each, and every workgroup
+// tracks at most 256 items of that launch too.  (The kernel uses them only
+// when the groups in range fill four rounds of the grid.)
+inline bool ffn_use_r320(long T, long top_k, long n_ffn, long d_ff, long G) {
+  const long groups = std::min(n_ffn, T * top_k / kR320Lo);
+  if (groups < 1 || G < 1) return false;
+  return big_items_per_wg_max(groups * big320_ntiles(d_ff), G) <= kBigMaxTilesPerWg;
 }
 
 }  // namespace plan

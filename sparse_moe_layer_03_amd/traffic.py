@@ -14,7 +14,10 @@
         KiB per KiB actually moved (the scale), the kernel's scaled bytes per
         launch, and a hash of the kernel's sources without comments (a
         reader of the summary can tell whether the kernel's code changed
-        since the counters were taken).
+        since the counters were taken).  When the regex matches several
+        kernels (one call of the operation launches each once), the figures
+        are per call: the sum over those kernels of their per-dispatch
+        medians.
 """
 
 from __future__ import annotations
@@ -63,33 +66,50 @@ def probe() -> None:
     print(f"copied {COPY_BYTES} bytes x3", flush=True)
 
 
-def per_dispatch(path, regex, counter):
-    vals = []
+def per_kernel(path, regex, counter):
+    """{kernel name: [counter value per dispatch]} for the kernels matching regex."""
+    vals = {}
     rx = re.compile(regex)
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
-                vals.append(float(r["Counter_Value"]))
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
     if not vals:
         raise SystemExit(f"no {counter} rows for /{regex}/ in {path}")
     return vals
 
 
+def per_dispatch(path, regex, counter):
+    return [v for vs in per_kernel(path, regex, counter).values() for v in vs]
+
+
 def summarize(a) -> None:
-    kf = per_dispatch(a.kernel_fetch, a.kernel_regex, "FETCH_SIZE")
-    kw = per_dispatch(a.kernel_write, a.kernel_regex, "WRITE_SIZE")
+    kf = per_kernel(a.kernel_fetch, a.kernel_regex, "FETCH_SIZE")
+    kw = per_kernel(a.kernel_write, a.kernel_regex, "WRITE_SIZE")
     cf = per_dispatch(a.copy_fetch, a.copy_regex, "FETCH_SIZE")
     cw = per_dispatch(a.copy_write, a.copy_regex, "WRITE_SIZE")
     kib = COPY_BYTES / 1024.0
     s_f = statistics.median(cf) / kib    # counter KiB per KiB really read
     s_w = statistics.median(cw) / kib
-    fetch_b = statistics.median(kf) * 1024.0 / s_f
-    write_b = statistics.median(kw) * 1024.0 / s_w
+    f_kib = sum(statistics.median(v) for v in kf.values())   # per call
+    w_kib = sum(statistics.median(v) for v in kw.values())
+    fetch_b = f_kib * 1024.0 / s_f
+    write_b = w_kib * 1024.0 / s_w
     lines = [
         f"# HBM traffic per launch of /{a.kernel_regex}/ (rocprofv3 --pmc, one counter per run)",
         f"# command: {a.command}",
-        f"kernel_fetch_kib_per_dispatch_median {statistics.median(kf):.1f}  (n={len(kf)})",
-        f"kernel_write_kib_per_dispatch_median {statistics.median(kw):.1f}  (n={len(kw)})",
+    ]
+    if len(kf) > 1:
+        lines.append(f"# {len(kf)} kernels per call; figures per call = sum of the per-kernel medians")
+        for name in sorted(kf):
+            lines.append(f"#   {name}: fetch {statistics.median(kf[name]):.1f} KiB, write "
+                         f"{statistics.median(kw.get(name, [0.0])):.1f} KiB per dispatch "
+                         f"(n={len(kf[name])})")
+    nf = sum(len(v) for v in kf.values())
+    nw = sum(len(v) for v in kw.values())
+    lines += [
+        f"kernel_fetch_kib_per_dispatch_median {f_kib:.1f}  (n={nf})",
+        f"kernel_write_kib_per_dispatch_median {w_kib:.1f}  (n={nw})",
         f"copy_fetch_kib_per_dispatch_median {statistics.median(cf):.1f}  (copy of {COPY_BYTES} B)",
         f"copy_write_kib_per_dispatch_median {statistics.median(cw):.1f}",
         f"scale_fetch {s_f:.4f}  scale_write {s_w:.4f}  (counter KiB per KiB moved)",

@@ -27,8 +27,8 @@ int main() {
   long T, k, N, Z, d, dff, bf16, gather, G;
   while (scanf("%ld %ld %ld %ld %ld %ld %ld %ld %ld", &T, &k, &N, &Z, &d, &dff, &bf16,
                &gather, &G) == 9) {
-    printf("%d %ld\n", (int)moe::plan::ffn_use_big(T, k, N, Z, d, dff, bf16 != 0, gather != 0, G),
-           moe::plan::big_mtiles_max(T * k, N));
+    printf("%d %ld %d\n", (int)moe::plan::ffn_use_big(T, k, N, Z, d, dff, bf16 != 0, gather != 0, G),
+           moe::plan::big_mtiles_max(T * k, N), (int)moe::plan::ffn_use_r320(T, k, N, dff, G));
   }
   return 0;
 }
@@ -54,9 +54,10 @@ def cdiv(a, b):
     return -(-a // b)
 
 
-def kernel_items_per_wg(counts, ntiles, G):
-    """Largest number of work items any workgroup runs, by the kernel's rules."""
-    mt = sum(cdiv(int(c), 256) for c in counts)
+def kernel_items_per_wg(counts, ntiles, G, rows=256):
+    """Largest number of work items any workgroup runs, by the kernel's rules
+    (m-tiles of `rows` rows per group)."""
+    mt = sum(cdiv(int(c), rows) for c in counts)
     tiles = mt * ntiles
     full = tiles - tiles % G
     rem = tiles - full
@@ -116,7 +117,7 @@ def test_many_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
     res = plan_driver(rows)
     rng = np.random.default_rng(G)
     n_big, most = 0, 0
-    for (T, k, N, Z, d, dff), (big, mt_max) in zip(SHAPES, res):
+    for (T, k, N, Z, d, dff), (big, mt_max, _) in zip(SHAPES, res):
         if not big:
             continue
         n_big += 1
@@ -150,3 +151,35 @@ def test_plan_refuses_shapes_past_the_limits(plan_driver):
     mt = res[4][1]
     assert cdiv(mt * 3, 256) > 256 and res[4][0] == 0
     assert res[5][0] == 1
+
+
+def counts_320(Tk, N, rng):
+    """Row spreads with as many groups of 257..320 rows as the rows allow."""
+    n = min(N, Tk // 257)
+    c = np.zeros(N, dtype=np.int64)
+    c[:n] = 257
+    c[0] += Tk - 257 * n          # the rest on one group (a 256-row tile group)
+    return [c, rng.multinomial(Tk, np.full(N, 1.0 / N))]
+
+
+@pytest.mark.parametrize("G", [256, 64, 8])
+def test_320_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
+    """When a shape's gate/up also uses the 320 x 192 tiles (experts of
+    257..320 rows), that launch's work items per workgroup stay within the
+    256 descriptor slots, and the 256-row launch's (which skips those
+    experts) too."""
+    rows = [(T, k, N, Z, d, dff, 1, 1, G) for (T, k, N, Z, d, dff) in SHAPES]
+    res = plan_driver(rows)
+    rng = np.random.default_rng(7 + G)
+    used = 0
+    for (T, k, N, Z, d, dff), (big, _, r320) in zip(SHAPES, res):
+        if not (big and r320):
+            continue
+        used += 1
+        for counts in counts_320(T * k, N, rng):
+            tall = [int(c) for c in counts if 257 <= c <= 320]
+            rest = [int(c) for c in counts if not 257 <= c <= 320]
+            assert kernel_items_per_wg(tall, cdiv(dff, 96), G, rows=320) <= 256
+            assert kernel_items_per_wg(rest, cdiv(dff, 128), G) <= 256
+    if G == 256:
+        assert used >= 3, used
