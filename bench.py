@@ -122,10 +122,12 @@ def gate_up_units(w, A, U):
 
 
 def down_kernel_name(w):
-    """The down GEMM's kernel for this shape (256x256 tiles only)."""
+    """The down GEMM's kernel for this shape."""
     name = gate_up_kernel_name(w)
     if name.startswith("grouped_gemm_big_kernel"):
-        return "grouped_gemm_big_kernel<2,4> (256x256 tiles, down)"
+        return ("grouped_gemm_big_kernel<2,4,*> (320x192 tiles for the experts of 257..320 rows "
+                "when they fill 4 rounds of the grid, then 256x256 tiles for the rest; down; "
+                "event time of both launches)")
     return (name.replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2")
             .replace("16x256", "16x128"))
 

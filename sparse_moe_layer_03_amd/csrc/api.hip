@@ -252,10 +252,9 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int
                       (hipStream_t)stream);
 }
 
-// Gate/up experts of 257..320 rows on the 320 x 192 tiles, where the shape
-// allows.
+// Experts of 257..320 rows on the 320 x 192 tiles, where the shape allows.
 static void set_r320(const moe_shape* s, GemmArgs& g, hipStream_t st) {
-  if (plan::ffn_use_r320(s->T, s->top_k, s->n_ffn, s->d_ff, big_grid(st))) {
+  if (plan::ffn_use_r320(s->T, s->top_k, s->n_ffn, s->d_model, s->d_ff, big_grid(st))) {
     g.r320_lo = plan::kR320Lo;
     g.r320_hi = plan::kR320Hi;
   }
@@ -307,7 +306,10 @@ int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down,
   g.top_k = s->top_k;
   g.M = s->T;
   g.ksplit = 1;
-  if (ffn_use_big(s, false, (hipStream_t)stream)) return launch_gemm_big(2, g, (hipStream_t)stream);
+  if (ffn_use_big(s, false, (hipStream_t)stream)) {
+    set_r320(s, g, (hipStream_t)stream);
+    return launch_gemm_big(2, g, (hipStream_t)stream);
+  }
   return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);
 }
 

@@ -29,12 +29,12 @@
 //    not all after the barrier: their issue stalls until earlier ones have
 //    drained into LDS, and eight waves issuing at once had kept every SIMD's
 //    MFMAs waiting for about a third of each step.
-//  * A second tile shape for gate/up, 320 x 192 on 16x16x32 MFMAs, takes the
-//    experts of 257..320 rows in one tile (a batch averaging 256 rows per
-//    expert has about half of them there); split into two 256-row tiles,
-//    each would stream the expert's whole weight slice through LDS.  Its own
-//    launch runs before the 256-row one, when those experts fill four rounds
-//    of the grid.
+//  * A second tile shape, 320 x 192 on 16x16x32 MFMAs, takes the experts of
+//    257..320 rows in one tile (a batch averaging 256 rows per expert has
+//    about half of them there); split into two 256-row tiles, each would
+//    stream the expert's whole weight slice through LDS.  Its own launch
+//    runs before the 256-row one, when those experts fill four rounds of the
+//    grid.
 //  * Balanced tile heights: an expert with m rows gets ceil(m / 256) tiles of
 //    equal height (a multiple of 32).  A wave runs the MFMAs of only the
 //    32-row blocks that hold rows: the K loop exists once per count of
@@ -120,7 +120,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
   static_assert(MODE != 1 || NB % 2 == 0, "gate/up pairing");
   static_assert(A_PW + 2 * B_PW < 64, "vmcnt range");
   static_assert(DPS * NKK == A_PW + B_PW, "DMA spread evenly over the slices");
-  static_assert(!R320 || MODE == 1, "320-row tiles: gate/up only");
+  static_assert(!R320 || MODE != 0, "320-row tiles: experts only");
   static_assert(HN % RPK == 0, "one DMA instruction's rows lie in one gate/up half");
   static_assert(BM * RB * 2 + BN * RB * 3 <= 160 * 1024, "LDS");
 
@@ -156,7 +156,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
   // the grid (their launch's partly idle last round costs up to one round);
   // both tile shapes count the groups alike.
   bool use320 = false;
-  if (MODE == 1 && g.r320_hi > 0) {
+  if (MODE != 0 && g.r320_hi > 0) {
     int n = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -166,7 +166,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     const int incl = block_inclusive_scan<NT>(n, s_scan);
     if (tid == NT - 1) s_scan[NT / 64] = incl;
     __syncthreads();
-    constexpr int HN320 = BigShape<true>::BN / 2;
+    constexpr int HN320 = MODE == 1 ? BigShape<true>::BN / 2 : BigShape<true>::BN;
     use320 = s_scan[NT / 64] * ((g.N + HN320 - 1) / HN320) >= 4 * (int)gridDim.x;
   }
   // m-tiles of a group of cnt rows on this kernel (none for the groups the
@@ -632,6 +632,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
         const int r = m0 + (i * WM + wm) * BLK + rin;
         if (r < m_end) {
           char* crow = (char*)g.c + (size_t)(row0 + r) * g.N * 2;
+          if (MODE == 1) {
 #pragma unroll
           for (int j = 0; j < NB / 2; ++j) {
             const int col = n0 + wn * (WTN / 2) + j * BLK + 4 * kg;
@@ -641,6 +642,15 @@ grouped_gemm_big_kernel(GemmArgs g) {
               *reinterpret_cast<uint2*>(crow + col * 2) =
                   bf16x4(swiglu(z[0], u[0]), swiglu(z[1], u[1]), swiglu(z[2], u[2]),
                          swiglu(z[3], u[3]));
+          }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              const int col = n0 + wn * WTN + j * BLK + 4 * kg;
+              const acc_t& v = acc[i][j];
+              if (col + 3 < g.N)
+                *reinterpret_cast<uint2*>(crow + col * 2) = bf16x4(v[0], v[1], v[2], v[3]);
+            }
           }
         }
       }
@@ -713,13 +723,13 @@ static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
   return check_launch();
 }
 
-// Expert modes: gate/up runs the groups of r320_lo..r320_hi rows on
-// 320 x 192 tiles and the others on 256 x 256 tiles (two launches on the
-// same stream; they write disjoint rows).
+// Expert modes: the groups of r320_lo..r320_hi rows on 320 x 192 tiles, the
+// others on 256 x 256 tiles (two launches on the same stream; they write
+// disjoint rows).
 template <int MODE>
 static int launch_big_expert(const GemmArgs& g, hipStream_t st) {
-  if (MODE == 1 && g.r320_hi > 0) {
-    const int rc = launch_big_mode<1, true>(g, st);
+  if (g.r320_hi > 0) {
+    const int rc = launch_big_mode<MODE, true>(g, st);
     if (rc != MOE_OK) return rc;
   }
   return launch_big_mode<MODE, false>(g, st);
@@ -732,7 +742,7 @@ int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
     if (g.ngroups != 1 || g.ksplit < 1 || (g.K / 64) % (2 * g.ksplit) != 0) return MOE_EINVAL;
     return launch_big_mode<0, false>(g, st);
   }
-  if (g.r320_hi > 0 && (mode != 1 || g.r320_lo < 1 || g.r320_hi > 320)) return MOE_EINVAL;
+  if (g.r320_hi > 0 && (g.r320_lo < 1 || g.r320_hi > 320)) return MOE_EINVAL;
   return mode == 1 ? launch_big_expert<1>(g, st) : launch_big_expert<2>(g, st);
 }
 

@@ -22,8 +22,8 @@ struct GemmArgs {
   int ngroups;             // experts (grouped modes)
   int top_k;
   int ksplit;              // router: K is split into this many partial sums
-  int r320_lo, r320_hi;    // many-row gate/up: groups of r320_lo..r320_hi rows
-                           // run on 320 x 192 tiles (r320_hi 0: none)
+  int r320_lo, r320_hi;    // many-row expert modes: groups of r320_lo..r320_hi
+                           // rows run on 320 x 192 tiles (r320_hi 0: none)
 };
 
 // mode: 0 router, 1 gate/up + SwiGLU, 2 down.  big: 128x128 tiles, else

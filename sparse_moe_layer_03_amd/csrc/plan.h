@@ -37,11 +37,13 @@ inline long big_ntiles(int mode, long d_model, long d_ff) {
   return mode == 1 ? cdiv(d_ff, kBigGateUpCols) : cdiv(d_model, kBigDownCols);
 }
 
-// In gate/up, experts with 257..320 rows run on a second tile shape,
-// 320 x 192 (96 H columns per tile), one tile each instead of two 256-row
-// tiles that would each stream the weight slice.
+// Experts with 257..320 rows run on a second tile shape, 320 x 192 (gate/up
+// tiles write 96 H columns, down tiles 192 output columns), one tile each
+// instead of two 256-row tiles that would each stream the weight slice.
 constexpr int kR320Lo = 257, kR320Hi = 320;
-inline long big320_ntiles(long d_ff) { return cdiv(d_ff, 96); }
+inline long big320_ntiles(int mode, long d_model, long d_ff) {
+  return mode == 1 ? cdiv(d_ff, 96) : cdiv(d_model, 192);
+}
 
 // Upper bound on the work items one workgroup of a G-workgroup grid runs.
 // The kernel's items are the tiles, except that a last round at most half
@@ -86,14 +88,15 @@ inline bool ffn_use_big(long T, long top_k, long n_ffn, long n_zero, long d_mode
   return big_items_per_wg_max(mt * nt, G) <= kBigMaxTilesPerWg;
 }
 
-// Whether a many-row gate/up also uses the 320-row tiles: at most
+// Whether a many-row shape also uses the 320-row tiles: at most
 // min(n_ffn, T*k / 257) groups take one such tile each, and every workgroup
-// tracks at most 256 items of that launch too.  (The kernel uses them only
-// when the groups in range fill four rounds of the grid.)
-inline bool ffn_use_r320(long T, long top_k, long n_ffn, long d_ff, long G) {
+// tracks at most 256 items of that launch too, in both modes.  (The kernel
+// uses them only when the groups in range fill four rounds of the grid.)
+inline bool ffn_use_r320(long T, long top_k, long n_ffn, long d_model, long d_ff, long G) {
   const long groups = std::min(n_ffn, T * top_k / kR320Lo);
   if (groups < 1 || G < 1) return false;
-  return big_items_per_wg_max(groups * big320_ntiles(d_ff), G) <= kBigMaxTilesPerWg;
+  const long nt = std::max(big320_ntiles(1, d_model, d_ff), big320_ntiles(2, d_model, d_ff));
+  return big_items_per_wg_max(groups * nt, G) <= kBigMaxTilesPerWg;
 }
 
 }  // namespace plan

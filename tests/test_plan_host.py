@@ -28,7 +28,7 @@ int main() {
   while (scanf("%ld %ld %ld %ld %ld %ld %ld %ld %ld", &T, &k, &N, &Z, &d, &dff, &bf16,
                &gather, &G) == 9) {
     printf("%d %ld %d\n", (int)moe::plan::ffn_use_big(T, k, N, Z, d, dff, bf16 != 0, gather != 0, G),
-           moe::plan::big_mtiles_max(T * k, N), (int)moe::plan::ffn_use_r320(T, k, N, dff, G));
+           moe::plan::big_mtiles_max(T * k, N), (int)moe::plan::ffn_use_r320(T, k, N, d, dff, G));
   }
   return 0;
 }
@@ -164,9 +164,9 @@ def counts_320(Tk, N, rng):
 
 @pytest.mark.parametrize("G", [256, 64, 8])
 def test_320_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
-    """When a shape's gate/up also uses the 320 x 192 tiles (experts of
-    257..320 rows), that launch's work items per workgroup stay within the
-    256 descriptor slots, and the 256-row launch's (which skips those
+    """When a shape also uses the 320 x 192 tiles (experts of 257..320 rows),
+    that launch's work items per workgroup stay within the 256 descriptor
+    slots in both modes, and the 256-row launch's (which skips those
     experts) too."""
     rows = [(T, k, N, Z, d, dff, 1, 1, G) for (T, k, N, Z, d, dff) in SHAPES]
     res = plan_driver(rows)
@@ -179,7 +179,8 @@ def test_320_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
         for counts in counts_320(T * k, N, rng):
             tall = [int(c) for c in counts if 257 <= c <= 320]
             rest = [int(c) for c in counts if not 257 <= c <= 320]
-            assert kernel_items_per_wg(tall, cdiv(dff, 96), G, rows=320) <= 256
-            assert kernel_items_per_wg(rest, cdiv(dff, 128), G) <= 256
+            for nt320, nt256 in ((cdiv(dff, 96), cdiv(dff, 128)), (cdiv(d, 192), cdiv(d, 256))):
+                assert kernel_items_per_wg(tall, nt320, G, rows=320) <= 256
+                assert kernel_items_per_wg(rest, nt256, G) <= 256
     if G == 256:
         assert used >= 3, used
