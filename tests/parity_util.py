@@ -145,7 +145,10 @@ def oracle_outputs_for_tokens(m: Model, x_dev, tokens, gpu_idx):
 def many_row_mtiles(offsets, n_ffn):
     """Sorted-position ranges [lo, hi) of the m-tiles the many-row expert
     GEMM cuts: expert e's c rows get ceil(c / 256) tiles of equal height,
-    rounded up to a multiple of 32 rows (the last tile takes the rest)."""
+    rounded up to a multiple of 32 rows (the last tile takes the rest).  An
+    expert of 257..320 rows that the 320-row launch takes as one tile gets
+    two ranges here; rows of both lie in that tile, so sampling them covers
+    it too."""
     tiles = []
     for e in range(n_ffn):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
