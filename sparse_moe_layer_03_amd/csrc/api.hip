@@ -141,8 +141,8 @@ static int ffn_big_tiles(const moe_shape* s) {
   return plan::ffn_tall_tiles(s->T, s->top_k, s->n_ffn, s->n_zero, s->d_model, s->d_ff);
 }
 
-// The many-row expert GEMMs (256x256 direct-to-LDS tiles); `gather`: gate/up
-// reads x through perm.
+// The many-row expert GEMMs (256x256 and 320x192 direct-to-LDS tiles);
+// `gather`: gate/up reads x through perm.
 static bool ffn_use_big(const moe_shape* s, bool gather, hipStream_t st) {
   return plan::ffn_use_big(s->T, s->top_k, s->n_ffn, s->n_zero, s->d_model, s->d_ff,
                            s->dtype == MOE_BF16, gather, big_grid(st));

@@ -30,9 +30,11 @@ struct GemmArgs {
 // 16-row tiles for few rows per expert.
 int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st);
 
-// bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles
-// (K a multiple of 128, at most 1024 groups, at most 128 tiles per
-// workgroup of the big_grid() launched: plan::ffn_use_big).
+// bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles,
+// and 320x192 tiles for the groups of r320_lo..r320_hi rows (K a multiple of
+// 128, at most 1024 groups, at most 256 tiles per workgroup of the
+// big_grid() launched: plan::ffn_use_big, plan::ffn_use_r320); mode 0: the
+// router GEMM.
 constexpr int kBigTileRows = 256;
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st);
 // Workgroups of a many-row launch on stream st (one per CU it may use).

@@ -65,7 +65,8 @@ inline bool ffn_tall_tiles(long T, long top_k, long n_ffn, long n_zero, long d_m
 }
 
 // Whether the expert GEMMs of a bf16 shape run on the many-row kernel
-// (256x256 direct-to-LDS tiles), for a grid of G workgroups.  `gather`:
+// (256x256 direct-to-LDS tiles, with 320x192 ones beside them:
+// ffn_use_r320), for a grid of G workgroups.  `gather`:
 // gate/up reads x rows through perm (token rows anywhere in x, addressed by
 // 32-bit offsets from x, so x must stay below 4 GiB); otherwise token rows
 // (x_perm or H) are contiguous per tile and addressed from a 64-bit tile
