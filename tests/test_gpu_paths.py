@@ -119,3 +119,48 @@ def test_expert_gemm_320_row_tiles(T, N, d, dff):
     # each case exercises the 320-row launch beside the 256-row one
     assert gate_up_320 or down_320
     assert (c < 257).sum() >= 1 and (c > 320).sum() >= 1
+
+
+@pytest.mark.parametrize("d,dff", [
+    (512, 4096),    # gate/up on 320-row tiles (43 n-tiles); down (3 n-tiles) on 256-row tiles
+    (6144, 256),    # down on 320-row tiles (32 n-tiles, K = 256); gate/up on 256-row tiles
+])
+def test_320_row_tiles_at_exact_row_counts(d, dff):
+    # Top-1 routing written by hand, so that expert row counts sit at the
+    # limits of the 320-row tiles: 256 (one 256-row tile), 257 and 320 (one
+    # 320-row tile), 321 (two 256-row tiles), 255, 1 and 0, and 33 more
+    # experts of 257..320 rows so that the 320-row launch runs (four rounds
+    # of the grid).  The expert GEMMs are fed by moe_dispatch and checked
+    # row by row against the oracle's.
+    import numpy as np
+    import torch
+    from oracle import moe_oracle as O
+    from sparse_moe_layer_03_amd import binding as B
+    from tests.parity_util import Model, row_rel_l2
+    counts = [256, 257, 320, 321, 0, 1, 255] + [257 + (7 * i) % 64 for i in range(33)]
+    N = len(counts)
+    rng = np.random.default_rng(31)
+    idx = np.repeat(np.arange(N), counts).astype(np.int32)
+    rng.shuffle(idx)
+    T = idx.size
+    w = S.Workload("rows320_exact", T=T, d_model=d, n_ffn=N, n_zero=0, d_ff=dff, top_k=1,
+                   dtype="bf16", seed=28)
+    G = B.moe_device_cu_count()
+    n320 = sum(257 <= c <= 320 for c in counts)
+    assert max(n320 * -(-dff // 96), n320 * -(-d // 192)) >= 4 * G
+    m = Model(w, "cuda")
+    x = S.make_x(w, 0, "cuda")
+    buf = B.LayerBuffers(m.shape, "cuda")
+    tidx = torch.as_tensor(idx.reshape(T, 1), device="cuda")
+    B.moe_dispatch(m.shape, tidx, x, buf.counts, buf.offsets, buf.perm, buf.inv_perm, None, buf.ws)
+    B.moe_expert_ffn(m.shape, x, None, buf.perm, buf.offsets, m.wg, m.wu, m.wd, buf.y_perm,
+                     buf.ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(buf.counts[:N].cpu().numpy(), counts)
+    ref = O.forward(S.to_numpy64(x), S.to_numpy64(m.wr), np.zeros(N, np.float32),
+                    S.to_numpy64(m.wg), S.to_numpy64(m.wu), S.to_numpy64(m.wd), N, 1, 1.0,
+                    topk_idx=idx.reshape(T, 1))
+    np.testing.assert_array_equal(buf.perm[:T].cpu().numpy(), ref["perm"])
+    err = row_rel_l2(S.to_numpy64(buf.y_perm[:T]), ref["y_perm"])
+    say(f"  T={T}, {n320} experts of 257..320 rows; y_perm row relL2 max {err.max():.3e}")
+    assert err.max() <= 1e-2
