@@ -124,6 +124,7 @@ def test_expert_gemm_320_row_tiles(T, N, d, dff):
 @pytest.mark.parametrize("d,dff", [
     (512, 4096),    # gate/up on 320-row tiles (43 n-tiles); down (3 n-tiles) on 256-row tiles
     (6144, 256),    # down on 320-row tiles (32 n-tiles, K = 256); gate/up on 256-row tiles
+    (6272, 256),    # down on 320-row tiles, 33 n-tiles, the last one 128 of 192 columns wide
 ])
 def test_320_row_tiles_at_exact_row_counts(d, dff):
     # Top-1 routing written by hand, so that expert row counts sit at the
