@@ -247,6 +247,27 @@ int moe_eplb_plan(const moe_shape* shape, int32_t n_slots, int32_t n_devices,
                   int32_t* slot_expert, int32_t* slot_rows, int32_t* slot_device,
                   int32_t* device_load, void* stream);
 
+/* moe_debug_checks -- the device-side index-range checks of the debug build.
+ * For callers debugging the library, not part of the layer: the library
+ * built with these checks (libmoe_mi355x_checks.so, same entry points) has
+ * every kernel test the index ranges it relies on; a failed check sets its
+ * bit below on the device that ran the kernel and the kernel continues with
+ * the access guarded, as the release build guards it.  This call waits for
+ * the current device (hipDeviceSynchronize), stores the OR of the bits set
+ * there since the last clearing call in *flags, and clears them if
+ * clear != 0.  Release builds: MOE_EUNSUPPORTED, *flags untouched.
+ * NULL flags: MOE_EINVAL; a HIP failure: MOE_EHIP. */
+#define MOE_CHECK_ROUTE_ID     (1u << 0) /* top-k wrote an expert id outside [0, E) */
+#define MOE_CHECK_DISPATCH_ID  (1u << 1) /* topk_idx given to dispatch outside [0, E) */
+#define MOE_CHECK_DISPATCH_POS (1u << 2) /* dispatch computed a position outside [0, T*k) */
+#define MOE_CHECK_GEMM_ROW     (1u << 3) /* expert GEMM: gathered token outside [0, T) */
+#define MOE_CHECK_GEMM_ITEMS   (1u << 4) /* expert GEMM: a workgroup got more work items
+                                            than it can track */
+#define MOE_CHECK_GEMM_TILE    (1u << 5) /* expert GEMM: a tile outside its expert's rows
+                                            or the output columns */
+#define MOE_CHECK_COMBINE_ROW  (1u << 6) /* combine: a slot's y_perm row outside [0, T*k) */
+int moe_debug_checks(uint32_t* flags, int clear);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # MOE_MI355X_LIB names another build of the same library (the host-only
 # sanitizer build that the host tests load); by default the in-tree one.
 LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(PKG, "libmoe_mi355x.so")
+# the debug build with device-side index-range checks (same entry points)
+LIB_CHECKS_PATH = os.path.join(PKG, "libmoe_mi355x_checks.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP",
@@ -27,7 +29,13 @@ STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP",
 ENTRY_POINTS = ("moe_workspace_bytes", "moe_strerror", "moe_device_cu_count", "moe_route",
                 "moe_dispatch", "moe_expert_ffn", "moe_ffn_gate_up", "moe_ffn_down",
                 "moe_combine", "moe_pid_update", "moe_balance_update", "moe_dispatch_noalloc",
-                "moe_eplb_plan")
+                "moe_eplb_plan", "moe_debug_checks")
+
+# bits of moe_debug_checks
+CHECK_BITS = {1 << 0: "MOE_CHECK_ROUTE_ID", 1 << 1: "MOE_CHECK_DISPATCH_ID",
+              1 << 2: "MOE_CHECK_DISPATCH_POS", 1 << 3: "MOE_CHECK_GEMM_ROW",
+              1 << 4: "MOE_CHECK_GEMM_ITEMS", 1 << 5: "MOE_CHECK_GEMM_TILE",
+              1 << 6: "MOE_CHECK_COMBINE_ROW"}
 
 
 class MoeShape(ctypes.Structure):
@@ -73,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.moe_balance_update.argtypes = [sp, ctypes.c_float, vp, vp, vp]
         L.moe_dispatch_noalloc.argtypes = [sp] + [vp] * 8
         L.moe_eplb_plan.argtypes = [sp, i32, i32] + [vp] * 8
+        L.moe_debug_checks.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
         for n in ENTRY_POINTS[3:]:
             getattr(L, n).restype = ctypes.c_int
         _lib = L
@@ -177,6 +186,14 @@ def moe_eplb_plan(shape, n_slots, n_devices, counts, offsets, replicas, slot_exp
            lib().moe_eplb_plan(ctypes.byref(shape), int(n_slots), int(n_devices), _p(counts),
                                _p(offsets), _p(replicas), _p(slot_expert), _p(slot_rows),
                                _p(slot_device), _p(device_load), _stream(stream)))
+
+
+def moe_debug_checks(clear=True) -> int:
+    """The failed device-check bits since the last clearing call (debug
+    build); raises MoeError with MOE_EUNSUPPORTED on a release build."""
+    v = ctypes.c_uint32(0)
+    _check("moe_debug_checks", lib().moe_debug_checks(ctypes.byref(v), 1 if clear else 0))
+    return int(v.value)
 
 
 class LayerBuffers:

@@ -15,6 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
+# debug build with the device-side index-range checks (moe_debug_checks)
+LIB_CHECKS = os.path.join(PKG, "libmoe_mi355x_checks.so")
+OBJ_CHECKS = os.path.join(PKG, "_build_checks")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "gemm.hip", "gemm_big.hip", "route.hip", "dispatch.hip", "combine.hip", "pid.hip",
@@ -43,7 +46,7 @@ SANITIZE_FLAGS = ["-O1", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
 
 def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-    flags = [f for f in CFLAGS if not (extra and f == "-O3")]
+    flags = [f for f in CFLAGS if not (any(x.startswith("-O") for x in extra) and f == "-O3")]
     cmd = [HIPCC, *flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
@@ -51,12 +54,17 @@ def _compile(src: str, obj_dir: str = OBJ, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, sanitize_out: str = "") -> str:
+def build(verbose: bool = False, sanitize_out: str = "", checks: bool = False) -> str:
     """Builds the library in-tree; with sanitize_out, builds the host-side
-    sanitizer build to that path instead."""
-    obj_dir = os.path.join(os.path.dirname(sanitize_out), "_obj") if sanitize_out else OBJ
-    extra = SANITIZE_FLAGS if sanitize_out else ()
-    lib = sanitize_out or LIB
+    sanitizer build to that path instead; with checks, the debug build with
+    the device-side index-range checks (LIB_CHECKS)."""
+    if sanitize_out:
+        obj_dir, extra, lib = os.path.join(os.path.dirname(sanitize_out), "_obj"), SANITIZE_FLAGS, \
+            sanitize_out
+    elif checks:
+        obj_dir, extra, lib = OBJ_CHECKS, ["-DMOE_DEVICE_CHECKS"], LIB_CHECKS
+    else:
+        obj_dir, extra, lib = OBJ, (), LIB
     os.makedirs(obj_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), SOURCES))
@@ -73,4 +81,6 @@ def build(verbose: bool = False, sanitize_out: str = "") -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    if "--checks" in sys.argv[1:]:
+        build(verbose=True, checks=True)
     sys.exit(0)

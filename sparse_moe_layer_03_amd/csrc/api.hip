@@ -378,4 +378,29 @@ int moe_eplb_plan(const moe_shape* s, int32_t n_slots, int32_t n_devices, const 
                      slot_rows, slot_device, device_load, (hipStream_t)stream);
 }
 
+int moe_debug_checks(uint32_t* flags, int clear) {
+#ifdef MOE_DEVICE_CHECKS
+  if (!flags) return MOE_EINVAL;
+  const hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    set_hip_error(e);
+    return MOE_EHIP;
+  }
+  unsigned (*const words[])(bool) = {check_word_route, check_word_dispatch, check_word_gemm,
+                                     check_word_gemm_big, check_word_combine};
+  uint32_t v = 0;
+  for (auto* fn : words) {
+    const unsigned w = fn(clear != 0);
+    if (w == ~0u) return MOE_EHIP;
+    v |= w;
+  }
+  *flags = v;
+  return MOE_OK;
+#else
+  (void)flags;
+  (void)clear;
+  return MOE_EUNSUPPORTED;
+#endif
+}
+
 }  // extern "C"

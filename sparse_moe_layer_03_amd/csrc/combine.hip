@@ -39,6 +39,9 @@ combine_kernel(const T* __restrict__ x, const T* __restrict__ y_perm,
       e = idx[a];
       g = gate[a];
       row = inv_perm[a];
+      // gridDim.x = T
+      const bool row_ok = (unsigned)row < gridDim.x * (unsigned)k;
+      if (e < n_ffn && !MOE_GUARD(row_ok, MOE_CHECK_COMBINE_ROW)) row = 0;
     }
     const bool ffn = lane < k && e < n_ffn;
     const uint64_t fb = __ballot(ffn);
@@ -98,6 +101,8 @@ combine_kernel(const T* __restrict__ x, const T* __restrict__ y_perm,
                                 reinterpret_cast<u32x4_t*>(y + xrow + c * CE));
   }
 }
+
+MOE_CHECK_ACCESSOR(check_word_combine)
 
 int launch_combine(int dtype, const void* x, const void* y_perm, const int32_t* idx,
                    const float* gate, const int32_t* inv_perm, int T, int d, int k, int n_ffn,

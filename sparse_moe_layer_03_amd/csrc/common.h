@@ -99,3 +99,45 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* s_tmp) {
   __syncthreads();
   return v + add;
 }
+
+// Device-side index-range checks of the debug build (-DMOE_DEVICE_CHECKS,
+// libmoe_mi355x_checks.so).  A failed check sets its bit (MOE_CHECK_* in
+// moe.h) in a word of the translation unit's device memory and the kernel
+// carries on with the access guarded as in the release build, so a check
+// never faults; moe_debug_checks reads and clears the words.  Release
+// builds compile every check out.
+#ifdef MOE_DEVICE_CHECKS
+static __device__ unsigned moe_check_word;
+__device__ __forceinline__ void moe_check_fail(unsigned bit) { atomicOr(&moe_check_word, bit); }
+#define MOE_CHECK(cond, bit)              \
+  do {                                    \
+    if (!(cond)) moe_check_fail(bit);     \
+  } while (0)
+// a check that also guards an access the release build makes unguarded
+__device__ __forceinline__ bool moe_guard(bool ok, unsigned bit) {
+  if (!ok) moe_check_fail(bit);
+  return ok;
+}
+#define MOE_GUARD(cond, bit) moe_guard((cond), (bit))
+// unsigned fn(bool clear): this translation unit's word (synchronous copy),
+// cleared afterwards if `clear`
+#define MOE_CHECK_ACCESSOR(fn)                                                            \
+  unsigned fn(bool clear) {                                                               \
+    unsigned v = 0;                                                                       \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(moe_check_word), sizeof v) != hipSuccess)      \
+      return ~0u;                                                                         \
+    if (clear) {                                                                          \
+      const unsigned z = 0;                                                               \
+      if (hipMemcpyToSymbol(HIP_SYMBOL(moe_check_word), &z, sizeof z) != hipSuccess)      \
+        return ~0u;                                                                       \
+    }                                                                                     \
+    return v;                                                                             \
+  }
+#else
+#define MOE_CHECK(cond, bit) \
+  do {                       \
+  } while (0)
+#define MOE_GUARD(cond, bit) true
+#define MOE_CHECK_ACCESSOR(fn) \
+  unsigned fn(bool) { return 0; }
+#endif

@@ -36,6 +36,7 @@ dispatch_hist_kernel(const int32_t* __restrict__ idx, int Tk, int E, int32_t* __
   __syncthreads();
   for (int a = lo + threadIdx.x; a < hi; a += kDispThreads) {
     const int e = idx[a];
+    MOE_CHECK((unsigned)e < (unsigned)E, MOE_CHECK_DISPATCH_ID);
     if ((unsigned)e < (unsigned)E) atomicAdd(&s_h[e], 1);  // ids are in range by contract
   }
   __syncthreads();
@@ -146,8 +147,10 @@ dispatch_scatter_kernel(const int32_t* __restrict__ idx, int Tk, int E,
     if (valid) {
       const int rank = __popcll(peers & lanemask_lt());
       const int pos = my[e] + rank;
-      perm[pos] = a;
-      inv_perm[a] = pos;
+      if (MOE_GUARD((unsigned)pos < (unsigned)Tk, MOE_CHECK_DISPATCH_POS)) {
+        perm[pos] = a;
+        inv_perm[a] = pos;
+      }
     }
     // the highest lane of each peer group advances that expert's cursor
     __builtin_amdgcn_wave_barrier();
@@ -181,6 +184,7 @@ dispatch_one_kernel(const int32_t* __restrict__ idx, int Tk, int E, int32_t* __r
   __syncthreads();
   for (int a = wlo + lane; a < whi; a += 64) {
     const int e = idx[a];
+    MOE_CHECK((unsigned)e < (unsigned)E, MOE_CHECK_DISPATCH_ID);
     if ((unsigned)e < (unsigned)E) atomicAdd(&s_w[w * E + e], 1);  // ids in range by contract
   }
   __syncthreads();
@@ -219,8 +223,10 @@ dispatch_one_kernel(const int32_t* __restrict__ idx, int Tk, int E, int32_t* __r
     if (valid) {
       const int rank = __popcll(peers & lanemask_lt());
       const int pos = my[ex] + rank;
-      perm[pos] = a;
-      inv_perm[a] = pos;
+      if (MOE_GUARD((unsigned)pos < (unsigned)Tk, MOE_CHECK_DISPATCH_POS)) {
+        perm[pos] = a;
+        inv_perm[a] = pos;
+      }
     }
     // the highest lane of each peer group advances that expert's cursor
     __builtin_amdgcn_wave_barrier();
@@ -269,12 +275,16 @@ gather_rows_kernel(const T* __restrict__ x, const int32_t* __restrict__ perm,
                    T* __restrict__ x_perm) {
   const int p = blockIdx.x;
   if (p >= offsets[n_ffn]) return;
+  // gridDim.x = T*k
+  if (!MOE_GUARD((unsigned)perm[p] < gridDim.x, MOE_CHECK_GEMM_ROW)) return;
   const int tok = perm[p] / k;
   constexpr int CE = 16 / sizeof(T);
   const char* src = (const char*)(x + (size_t)tok * d);
   char* dst = (char*)(x_perm + (size_t)p * d);
   for (int c = threadIdx.x; c < d / CE; c += 256) st16(dst + c * 16, ld16(src + c * 16));
 }
+
+MOE_CHECK_ACCESSOR(check_word_dispatch)
 
 int launch_gather(int dtype, const void* x, const int32_t* perm, const int32_t* offsets,
                   int n_ffn, int Tk, int k, int d, void* x_perm, hipStream_t st) {

@@ -166,6 +166,7 @@ grouped_gemm_kernel(GemmArgs g) {
     const int rows = (MODE == MODE_ROUTER) ? g.M : (g.offsets[grp + 1] - row0);
     const int m0 = mi * BM;
     const int n0 = nt * HN;
+    MOE_CHECK(grp < ngroups && mi < mt_g && m0 < rows && n0 < g.N, MOE_CHECK_GEMM_TILE);
     tl.split = split;
     tl.rot = K_ROTATE ? (int)(((long)grp * ntiles + nt) % nK) : 0;
     tl.row0 = row0;
@@ -184,6 +185,7 @@ grouped_gemm_kernel(GemmArgs g) {
       else if (MODE == MODE_GATE_UP && g.perm != nullptr)
       {
         src_row = g.perm[row0 + rr] / g.top_k;  // gather token rows on load
+        MOE_CHECK(src_row >= 0 && src_row < g.M, MOE_CHECK_GEMM_ROW);
         if (src_row < 0 || src_row >= g.M) src_row = 0;
       }
       else
@@ -356,6 +358,8 @@ grouped_gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------- launch --
+
+MOE_CHECK_ACCESSOR(check_word_gemm)
 
 template <typename T, int MODE, int BM, int BN, int WM, int WN>
 static int launch_cfg(const GemmArgs& g, hipStream_t st) {

@@ -239,6 +239,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
   for (int k = 0; vid + k * G < total; ++k) {
     // the host bounds the items per workgroup by 64 * kBigDescRegs (the
     // descriptor registers); never read past them
+    MOE_CHECK(MODE == 0 || k < 64 * kBigDescRegs, MOE_CHECK_GEMM_ITEMS);
     if (MODE != 0 && k >= 64 * kBigDescRegs) break;
     const int tsplit = (MODE == 0) ? (vid + k * G) / tiles : 0;
     const int it = vid + k * G - tsplit * tiles;  // item (== tile unless sliced)
@@ -275,6 +276,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
       if (m0 >= m_end) continue;
     }
     const int n0 = nt * HN;
+    MOE_CHECK(grp < ngroups && mi < mt_g && m0 < m_end && m_end <= cnt && n0 < g.N &&
+                  m_end - m0 <= BM,
+              MOE_CHECK_GEMM_TILE);
     // row blocks of this wave that hold rows: i with (i*WM + wm)*BLK < rows
     const int nrb = (m_end - m0 + BLK - 1) / BLK;
     const int mba = min(MB, (nrb - wm + WM - 1) / WM);
@@ -296,6 +300,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       long src_row;
       if (gather) {
         src_row = g.perm[row0 + rr] / g.top_k;  // gather token rows on load
+        MOE_CHECK(src_row >= 0 && src_row < g.M, MOE_CHECK_GEMM_ROW);
         if (src_row < 0 || src_row >= g.M) src_row = 0;
       } else {
         src_row = rr - m0;
@@ -708,6 +713,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
 #ifndef MOE_BIG_MG
 #define MOE_BIG_MG 4
 #endif
+
+MOE_CHECK_ACCESSOR(check_word_gemm_big)
 
 int big_grid(hipStream_t st) {
   int grid = st == nullptr ? device_cu_count() : stream_cu_count(st);  // one workgroup per CU

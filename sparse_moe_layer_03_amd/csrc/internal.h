@@ -90,6 +90,14 @@ int check_launch();
 // Records a HIP error for moe_strerror (this thread).
 void set_hip_error(hipError_t e);
 
+// Device-check words of the kernels' translation units (debug build; 0 in
+// release builds, ~0u on a HIP failure), cleared after reading if `clear`.
+unsigned check_word_route(bool clear);
+unsigned check_word_dispatch(bool clear);
+unsigned check_word_gemm(bool clear);
+unsigned check_word_gemm_big(bool clear);
+unsigned check_word_combine(bool clear);
+
 // moe_dispatch's argument checks (no workspace) and its launches with the
 // per-block histogram `hist` ([E, dispatch_blocks(T*k)] int32).
 int dispatch_checks(const moe_shape* s, const int32_t* topk_idx, const void* x, int32_t* counts,

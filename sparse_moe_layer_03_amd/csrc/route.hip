@@ -119,8 +119,11 @@ __device__ __forceinline__ void select_topk(float (&l)[NT][PL], float (&m)[NT],
       const uint64_t bal = __ballot(sel[n][i]);
       if (sel[n][i] && t[n] >= 0) {
         const int o = t[n] * k + pos + __popcll(bal & lanemask_lt());
-        idx[o] = lane + 64 * i;
-        gate[o] = scaling * p[n][i];
+        MOE_CHECK(lane + 64 * i < E, MOE_CHECK_ROUTE_ID);
+        if (MOE_GUARD(o < (t[n] + 1) * k, MOE_CHECK_ROUTE_ID)) {  // at most k per token
+          idx[o] = lane + 64 * i;
+          gate[o] = scaling * p[n][i];
+        }
       }
       pos += __popcll(bal);
     }
@@ -380,6 +383,8 @@ int launch_topk(const float* partials, int nsplit, const float* col_bias, float*
 #undef MOE_TOPK_ARGS
   return check_launch();
 }
+
+MOE_CHECK_ACCESSOR(check_word_route)
 
 // Split the router's K loop until there are about 1024 (tile, split) work
 // items, keeping at least two K-steps per split; the split count divides the

@@ -22,11 +22,28 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(B.ENTRY_POINTS)
     L = B.lib()
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_debug_checks_build_exports_the_same_symbols():
+    # the debug build with device-side index-range checks is a drop-in copy
+    # of the release library
+    assert os.path.exists(B.LIB_CHECKS_PATH), "build it with build(checks=True)"
+    L = ctypes.CDLL(B.LIB_CHECKS_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    L.moe_debug_checks.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    assert L.moe_debug_checks(None, 1) == -1            # MOE_EINVAL before any GPU work
+
+
+def test_debug_checks_unsupported_in_the_release_build():
+    v = ctypes.c_uint32(7)
+    assert B.lib().moe_debug_checks(ctypes.byref(v), 1) == -2   # MOE_EUNSUPPORTED
+    assert v.value == 7
 
 
 def test_workspace_bytes():
