@@ -131,3 +131,37 @@ def test_moe_and_dense_on_cu_partitioned_streams_match_serial(dense_cus, pattern
     finally:
         ms.close()
         ds.close()
+
+
+@pytest.mark.parametrize("cus", [64, 32])
+def test_many_row_gemms_on_a_cu_masked_stream_match_the_full_chip(cus):
+    # The whole layer on a stream restricted to `cus` contiguous CUs: the
+    # persistent expert GEMMs (256x256 and 320x192 tiles; 38 of 48 experts
+    # hold 257..320 rows) size their grids by the stream's CU mask, so the
+    # tiles land on other workgroups and the last round is cut differently,
+    # and the outputs still equal the full-chip run bit for bit.
+    w = S.Workload("rows320", T=3480, d_model=512, n_ffn=48, n_zero=0, d_ff=4096, top_k=4,
+                   dtype="bf16", bias_var=0.0, seed=27)
+    say(f"layer on a {cus}-CU stream vs the full chip")
+    m = Model(w)
+    x = S.make_x(w, 0, "cuda")
+    buf = B.LayerBuffers(m.shape, "cuda")
+    gpu, _ = run_gpu(m, x, buf, with_logits=False)
+    c = gpu["counts"][:w.n_ffn]
+    assert ((c >= 257) & (c <= 320)).sum() * -(-w.d_ff // 96) >= 4 * cus
+    y_full = buf.y.clone()
+    n = B.moe_device_cu_count()
+    ms = scmoe.MaskedStream(scmoe.cu_mask(n, 0, cus, "contiguous"))
+    try:
+        assert ms.cus == cus
+        main = torch.cuda.current_stream()
+        for rep in range(2):
+            buf.y.zero_()
+            ms.stream.wait_stream(main)
+            with torch.cuda.stream(ms.stream):
+                B.layer_forward(buf, x, m.wr, m.bias, m.wg, m.wu, m.wd, stream=ms.stream)
+            main.wait_stream(ms.stream)
+            torch.cuda.synchronize()
+            assert torch.equal(buf.y, y_full), rep
+    finally:
+        ms.close()
