@@ -276,6 +276,23 @@ grouped_gemm_big_kernel(GemmArgs g) {
       if (m0 >= m_end) continue;
     }
     const int n0 = nt * HN;
+    // Down tiles walk their K range from a step rotated by (expert, n-tile):
+    // the rows of W_down lie 4 KiB apart, and tiles that all read the same
+    // K-step of their weight rows crowd the same HBM channels (prefill down
+    // 4.02 -> 3.84 ms; gate/up, rows 12 KiB apart, gained nothing).  All
+    // m-tiles of one (expert, n-tile) share the rotation, and so their weight
+    // stages in L2; a tile's accumulation order depends only on its (expert,
+    // n-tile), so results stay deterministic.
+    const int rot = (MODE == 2) ? (int)(((long)grp * ntiles + nt) % nK) : 0;
+    auto kofs = [&](int kstep) -> size_t {
+      if constexpr (MODE == 2) {
+        int kr = kstep + rot;
+        if (kr >= nK) kr -= nK;
+        return (size_t)kr * RB;
+      } else {
+        return (size_t)kstep * RB;
+      }
+    };
     MOE_CHECK(grp < ngroups && mi < mt_g && m0 < m_end && m_end <= cnt && n0 < g.N &&
                   m_end - m0 <= BM,
               MOE_CHECK_GEMM_TILE);
@@ -345,7 +362,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     // past the tile were clamped to its last row above.
     auto issue_a = [&](auto sc, int ks) {
       char* sa = stage_a(sc);
-      const size_t off = (size_t)ks * RB;
+      const size_t off = kofs(ks);
 #pragma unroll
       for (int q = 0; q < A_PW; ++q)
         __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
@@ -353,7 +370,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     };
     auto issue_b = [&](auto sc, int ks) {
       char* sb = stage_b(sc);
-      const size_t off = (size_t)ks * RB;
+      const size_t off = kofs(ks);
 #pragma unroll
       for (int q = 0; q < B_PW; ++q) {
         const char* bb = up_half(q) ? b_base1 : b_base0;
@@ -416,13 +433,13 @@ grouped_gemm_big_kernel(GemmArgs g) {
       auto dma_one = [&](int L) {
         if (L < A_PW) {
           char* sa2 = stage_a(std::integral_constant<int, (AS + 1) % 2>{});
-          const size_t off = (size_t)(R320 ? min(ks + 1, nK - 1) : ks + 1) * RB;
+          const size_t off = kofs(R320 ? min(ks + 1, nK - 1) : ks + 1);
           __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[L] + off),
                                            (lds_void_t*)(sa2 + (wave + L * NW) * 1024), 16, 0, 0);
         } else {
           const int q = L - A_PW;
           char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
-          const size_t off = (size_t)(R320 ? min(ks + 2, nK - 1) : ks + 2) * RB;
+          const size_t off = kofs(R320 ? min(ks + 2, nK - 1) : ks + 2);
           const char* bb = up_half(q) ? b_base1 : b_base0;
           __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
                                            (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, 0);
