@@ -1,6 +1,8 @@
-"""Builds libmoe_mi355x.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Builds libmoe_mi355x.so (the C-ABI library) and its debug build with
+device-side index-range checks, libmoe_mi355x_checks.so, in-tree with hipcc
+for gfx950.
 
-    python -m sparse_moe_layer_03_amd.build
+    python -m sparse_moe_layer_03_amd.build [--release-only]
 """
 
 from __future__ import annotations
@@ -81,6 +83,6 @@ def build(verbose: bool = False, sanitize_out: str = "", checks: bool = False) -
 
 if __name__ == "__main__":
     build(verbose=True)
-    if "--checks" in sys.argv[1:]:
+    if "--release-only" not in sys.argv[1:]:
         build(verbose=True, checks=True)
     sys.exit(0)
