@@ -125,9 +125,9 @@ def down_kernel_name(w):
     """The down GEMM's kernel for this shape."""
     name = gate_up_kernel_name(w)
     if name.startswith("grouped_gemm_big_kernel"):
-        return ("grouped_gemm_big_kernel<2,4,*> (320x192 tiles for the experts of 257..320 rows "
-                "when they fill 4 rounds of the grid, then 256x256 tiles for the rest; down; "
-                "event time of both launches)")
+        return ("grouped_gemm_big_kernel<2,4,1|2> (320x192 tiles for the experts of 257..320 "
+                "rows when they fill 4 rounds of the grid, then 256x256 tiles on 16x16x32 MFMAs "
+                "for the rest; down; event time of both launches)")
     return (name.replace("gate/up + SwiGLU", "down").replace("mode 1", "mode 2")
             .replace("16x256", "16x128"))
 
@@ -145,8 +145,8 @@ def gate_up_kernel_name(w):
             or Tk // w.n_ffn >= 64)
     if (tall and w.dtype == "bf16" and w.d_model % 128 == 0 and w.d_ff % 128 == 0
             and cdiv(Tk, 256) * min(w.d_ff // 128, w.d_model // 256) >= 64):
-        return ("grouped_gemm_big_kernel<1,4,*> (320x192 tiles for the experts of 257..320 rows "
-                "when they fill 4 rounds of the grid, then 256x256 tiles for the rest; "
+        return ("grouped_gemm_big_kernel<1,4,1|0> (320x192 tiles for the experts of 257..320 "
+                "rows when they fill 4 rounds of the grid, then 256x256 tiles for the rest; "
                 "gate/up + SwiGLU; event time of both launches)")
     if tall:
         return "grouped_gemm_kernel mode 1 (128x128 tiles, gate/up + SwiGLU)"

@@ -34,7 +34,8 @@
 //    about half of them there); split into two 256-row tiles, each would
 //    stream the expert's whole weight slice through LDS.  Its own launch
 //    runs before the 256-row one, when those experts fill four rounds of the
-//    grid.
+//    grid.  The down GEMM's 256 x 256 tiles run on 16x16x32 MFMAs as well
+//    (16-row blocks: half the padding of the 32-row ones).
 //  * Balanced tile heights: an expert with m rows gets ceil(m / 256) tiles of
 //    equal height (a multiple of 32).  A wave runs the MFMAs of only the
 //    32-row blocks that hold rows: the K loop exists once per count of
@@ -81,17 +82,25 @@ static_assert(kBigMaxGroups == plan::kBigMaxGroups && kBigTileRows == plan::kBig
               "host plan matches the kernel");
 static_assert(plan::kR320Lo > kBigTileRows && plan::kR320Hi <= 320, "320-row tiles");
 
-// The two tile shapes.  256 x 256 on 32x32x16 MFMAs, 8 waves of 128 x 64:
-// every expert except those with 257..320 rows.  320 x 192 on 16x16x32
-// MFMAs, 8 waves of 80 x 96 (120 accumulators per lane, 152 KiB of LDS):
-// an expert with 257..320 rows in one tile instead of two, so its weight
-// slice passes through LDS once.
-template <bool R320>
+// The tile shapes.
+//  0: 256 x 256 on 32x32x16 MFMAs, 8 waves of 128 x 64: the router, and the
+//     gate/up experts outside 257..320 rows.
+//  1: 320 x 192 on 16x16x32 MFMAs, 8 waves of 80 x 96 (120 accumulators per
+//     lane, 152 KiB of LDS): an expert with 257..320 rows in one tile
+//     instead of two, so its weight slice passes through LDS once.
+//  2: 256 x 256 on 16x16x32 MFMAs, 8 waves of 64 x 128: the down experts
+//     outside 257..320 rows.  Rows come in blocks of 16, so a tile's last
+//     block carries 8 padding rows on average instead of 16, and it ran
+//     faster than shape 0 for down on every workload (prefill 3.83 -> 3.73
+//     ms); for gate/up it was slower on the skewed and small batches.  Its
+//     fragments are read once per K-slice (a second set does not fit next
+//     to 128 accumulators).
+template <int SHAPE>
 struct BigShape {
-  static constexpr int BM = R320 ? 320 : 256, BN = R320 ? 192 : 256;
-  static constexpr int WM = R320 ? 4 : 2, WN = R320 ? 2 : 4;
-  static constexpr int BLK = R320 ? 16 : 32;  // rows and weight rows per MFMA block
-  static constexpr int KSL = R320 ? 32 : 16;  // K per MFMA
+  static constexpr int BM = SHAPE == 1 ? 320 : 256, BN = SHAPE == 1 ? 192 : 256;
+  static constexpr int WM = SHAPE == 0 ? 2 : 4, WN = SHAPE == 0 ? 4 : 2;
+  static constexpr int BLK = SHAPE == 0 ? 32 : 16;  // rows and weight rows per MFMA block
+  static constexpr int KSL = SHAPE == 0 ? 16 : 32;  // K per MFMA
 };
 
 // Whether a group of `cnt` rows runs on the 320-row kernel (both kernels
@@ -100,10 +109,11 @@ __device__ __forceinline__ bool rows320(const GemmArgs& g, int cnt) {
   return g.r320_hi > 0 && cnt >= g.r320_lo && cnt <= g.r320_hi && cnt <= 320;
 }
 
-template <int MODE, int MG, bool R320>
+template <int MODE, int MG, int SHAPE>
 __global__ void __launch_bounds__(512, 1)
 grouped_gemm_big_kernel(GemmArgs g) {
-  using SH = BigShape<R320>;
+  constexpr bool R320 = SHAPE == 1;
+  using SH = BigShape<SHAPE>;
   constexpr int BM = SH::BM, BN = SH::BN, WM = SH::WM, WN = SH::WN, NW = WM * WN, NT = 64 * NW;
   constexpr int BLK = SH::BLK;
   constexpr int RB = 128;                           // bytes per stage row
@@ -116,11 +126,12 @@ grouped_gemm_big_kernel(GemmArgs g) {
   constexpr int B_PW = BN / RPK / NW;
   constexpr int NKK = KS / SH::KSL;                 // MFMA K-slices per stage
   constexpr int DPS = (A_PW + B_PW) / NKK;          // DMA instructions per slice
-  using acc_t = std::conditional_t<R320, f32x4_t, f32x16_t>;
+  constexpr bool B16 = SH::BLK == 16;  // 16x16x32 MFMAs, all K-steps in kloop
+  using acc_t = std::conditional_t<B16, f32x4_t, f32x16_t>;
   static_assert(MODE != 1 || NB % 2 == 0, "gate/up pairing");
   static_assert(A_PW + 2 * B_PW < 64, "vmcnt range");
   static_assert(DPS * NKK == A_PW + B_PW, "DMA spread evenly over the slices");
-  static_assert(!R320 || MODE != 0, "320-row tiles: experts only");
+  static_assert(!B16 || MODE != 0, "16x16 tiles: experts only");
   static_assert(HN % RPK == 0, "one DMA instruction's rows lie in one gate/up half");
   static_assert(BM * RB * 2 + BN * RB * 3 <= 160 * 1024, "LDS");
 
@@ -331,7 +342,8 @@ grouped_gemm_big_kernel(GemmArgs g) {
     // second; the 8 rows one DMA instruction fills lie in one half (with 256
     // rows the half is fixed per q, with 192 it depends on the wave)
     auto up_half = [&](int q) {
-      return MODE == 1 && (R320 ? (wave + q * NW) * RPK >= HN : (q * NW) * RPK >= HN);
+      return MODE == 1 && (HN % (NW * RPK) != 0 ? (wave + q * NW) * RPK >= HN
+                                                 : (q * NW) * RPK >= HN);
     };
     uint32_t b_off[B_PW];
 #pragma unroll
@@ -433,13 +445,13 @@ grouped_gemm_big_kernel(GemmArgs g) {
       auto dma_one = [&](int L) {
         if (L < A_PW) {
           char* sa2 = stage_a(std::integral_constant<int, (AS + 1) % 2>{});
-          const size_t off = kofs(R320 ? min(ks + 1, nK - 1) : ks + 1);
+          const size_t off = kofs(B16 ? min(ks + 1, nK - 1) : ks + 1);
           __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[L] + off),
                                            (lds_void_t*)(sa2 + (wave + L * NW) * 1024), 16, 0, 0);
         } else {
           const int q = L - A_PW;
           char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
-          const size_t off = kofs(R320 ? min(ks + 2, nK - 1) : ks + 2);
+          const size_t off = kofs(B16 ? min(ks + 2, nK - 1) : ks + 2);
           const char* bb = up_half(q) ? b_base1 : b_base0;
           __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
                                            (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, 0);
@@ -452,15 +464,18 @@ grouped_gemm_big_kernel(GemmArgs g) {
       auto frag = [&](const char* base, int r, int c) {
         return *reinterpret_cast<const u32x4_t*>(&base[r * RB + (swz(r, c) << 4)]);
       };
-      if constexpr (R320) {
-        // Two K-slices of 32 per stage.  Slice 0's fragments are read after
-        // the barrier; slice 1's under slice 0's MFMAs, which run token-row
-        // block by block (i-major): each token-row fragment of slice 1 once
-        // slice 0's last MFMA on that block has issued, the weight fragments
-        // one by one in the last block, so each can take the registers of
-        // the fragment it replaces (120 accumulators leave no room for a
-        // second fragment set).  A scheduling fence closes every block's
-        // group; the slice's DMA loads are spread over the groups.
+      if constexpr (B16) {
+        // Two K-slices of 32 per stage, MFMAs token-row block by block
+        // (i-major), a scheduling fence closing every block's group, the
+        // slice's DMA loads spread over the groups.
+        // Shape 1: slice 0's fragments are read after the barrier, slice 1's
+        // under slice 0's MFMAs: each token-row fragment once slice 0's last
+        // MFMA on that block has issued, the weight fragments one by one in
+        // the last block, so each can take the registers of the fragment it
+        // replaces (120 accumulators leave no room for a second set).
+        // Shape 2 (128 accumulators, 12 fragments per slice): each slice
+        // reads its fragments, then runs its MFMAs.
+        if constexpr (SHAPE == 1) {
         u32x4_t a0[MBA], a1[MBA], w0[NB], w1[NB];
 #pragma unroll
         for (int i = 0; i < MBA; ++i) a0[i] = frag(sa, (i * WM + wm) * BLK + rin, kg);
@@ -503,6 +518,37 @@ grouped_gemm_big_kernel(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
           }
         }
+        } else {
+        u32x4_t a0[MBA], w0[NB];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+          for (int i = 0; i < MBA; ++i) a0[i] = frag(sa, (i * WM + wm) * BLK + rin, 4 * kk + kg);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) w0[j] = frag(sb, brow(j), 4 * kk + kg);
+          __builtin_amdgcn_sched_group_barrier(0x100, MBA + NB, 0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < MBA; ++i) {
+            const int d_lo = (i * DPS + MBA - 1) / MBA, d_hi = ((i + 1) * DPS + MBA - 1) / MBA;
+            if constexpr (SPREAD) {
+#pragma unroll
+              for (int d = d_lo; d < d_hi; ++d) dma_one(kk * DPS + d);
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, w0[j]), __builtin_bit_cast(bf16x8_t, a0[i]),
+                  acc[i][j], 0, 0, 0);
+            if constexpr (SPREAD) {
+#pragma unroll
+              for (int d = d_lo; d < d_hi; ++d) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        }
       } else {
       u32x4_t af[2][MBA], bfr[2][NB];
       auto load = [&](int set, int kk) {
@@ -512,7 +558,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) bfr[set][j] = frag(sb, brow(j), c);
       };
-      static_assert(R320 || !SPREAD || (A_PW == 4 && B_PW == 4 && NKK == 4), "two DMA loads per slice");
+      static_assert(B16 || !SPREAD || (A_PW == 4 && B_PW == 4 && NKK == 4), "two DMA loads per slice");
       // Pin the schedule (the default one sinks every LDS read next to its
       // first use and stalls on it): the first slice's reads, then each
       // slice's MFMAs with the next slice's reads interleaved 1:1 at the
@@ -584,7 +630,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       int ks = 0;
       // 320-row tiles run every step here, the last ones refilling stages
       // that are never read (the refill K-step is clamped to the last one)
-      for (; ks + (R320 ? 6 : 8) <= nK; ks += 6) {
+      for (; ks + (B16 ? 6 : 8) <= nK; ks += 6) {
         kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
         kstep(mbac, I1{}, I1{}, T{}, T{}, ks + 1);
         kstep(mbac, I0{}, I2{}, T{}, T{}, ks + 2);
@@ -592,7 +638,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
         kstep(mbac, I0{}, I1{}, T{}, T{}, ks + 4);
         kstep(mbac, I1{}, I2{}, T{}, T{}, ks + 5);
       }
-      if constexpr (R320) {
+      if constexpr (B16) {
         // nK is even: 0, 2 or 4 steps remain
         if (ks + 2 <= nK) {
           kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
@@ -608,14 +654,14 @@ grouped_gemm_big_kernel(GemmArgs g) {
     // a wave with no rows (mba == 0) still loads and waits with the others;
     // its one block of clamped rows is never stored
     int ks;
-    if (R320 && mba >= 5) ks = kloop(std::integral_constant<int, R320 ? 5 : 4>{});
+    if (MB >= 5 && mba >= 5) ks = kloop(std::integral_constant<int, MB >= 5 ? 5 : 4>{});
     else if (mba >= 4) ks = kloop(std::integral_constant<int, 4>{});
     else if (mba == 3) ks = kloop(std::integral_constant<int, 3>{});
     else if (mba == 2) ks = kloop(std::integral_constant<int, 2>{});
     else ks = kloop(std::integral_constant<int, 1>{});
     // The last 2, 4 or 6 steps run every block (one copy of the code; blocks
     // without rows are never stored) with refills decided at run time.
-    if constexpr (!R320) {
+    if constexpr (!B16) {
       using M4 = std::integral_constant<int, MB>;
       kstep(M4{}, I0{}, I0{}, ks + 1 < nK, ks + 2 < nK, ks);
       kstep(M4{}, I1{}, I1{}, ks + 2 < nK, ks + 3 < nK, ks + 1);
@@ -648,7 +694,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
       const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504f));
       return z * sg * u;
     };
-    if constexpr (R320) {
+    if constexpr (B16) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) {
         const int r = m0 + (i * WM + wm) * BLK + rin;
@@ -731,6 +777,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
 #define MOE_BIG_MG 4
 #endif
 
+
 MOE_CHECK_ACCESSOR(check_word_gemm_big)
 
 int big_grid(hipStream_t st) {
@@ -739,9 +786,9 @@ int big_grid(hipStream_t st) {
   return grid < 8 ? 8 : grid;
 }
 
-template <int MODE, bool R320>
+template <int MODE, int SHAPE>
 static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
-  auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG, R320>;
+  auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG, SHAPE>;
   if (device_cu_count() <= 0) return MOE_EHIP;
   hipLaunchKernelGGL(kern, dim3(big_grid(st)), dim3(512), 0, st, g);
   return check_launch();
@@ -753,10 +800,10 @@ static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
 template <int MODE>
 static int launch_big_expert(const GemmArgs& g, hipStream_t st) {
   if (g.r320_hi > 0) {
-    const int rc = launch_big_mode<MODE, true>(g, st);
+    const int rc = launch_big_mode<MODE, 1>(g, st);
     if (rc != MOE_OK) return rc;
   }
-  return launch_big_mode<MODE, false>(g, st);
+  return launch_big_mode<MODE, MODE == 2 ? 2 : 0>(g, st);
 }
 
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
@@ -764,7 +811,7 @@ int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
   if (mode == 0) {
     // each split covers an even number (>= 2) of 64-wide K-steps
     if (g.ngroups != 1 || g.ksplit < 1 || (g.K / 64) % (2 * g.ksplit) != 0) return MOE_EINVAL;
-    return launch_big_mode<0, false>(g, st);
+    return launch_big_mode<0, 0>(g, st);
   }
   if (g.r320_hi > 0 && (g.r320_lo < 1 || g.r320_hi > 320)) return MOE_EINVAL;
   return mode == 1 ? launch_big_expert<1>(g, st) : launch_big_expert<2>(g, st);
