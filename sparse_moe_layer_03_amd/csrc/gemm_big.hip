@@ -56,6 +56,9 @@
 
 namespace moe {
 
+// cache-policy operand of a load: non-temporal
+constexpr int kCpolNT = 2;
+
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -380,14 +383,17 @@ grouped_gemm_big_kernel(GemmArgs g) {
         __builtin_amdgcn_global_load_lds((glb_void_t*)(a_base + a_off[q] + off),
                                          (lds_void_t*)(sa + (wave + q * NW) * 1024), 16, 0, 0);
     };
-    auto issue_b = [&](auto sc, int ks) {
+    // ntc: whether the weight loads are non-temporal (an expert's weight
+    // slice read by one m-tile only)
+    auto issue_b = [&](auto sc, int ks, auto ntc) {
+      constexpr int CP = decltype(ntc)::value ? kCpolNT : 0;
       char* sb = stage_b(sc);
       const size_t off = kofs(ks);
 #pragma unroll
       for (int q = 0; q < B_PW; ++q) {
         const char* bb = up_half(q) ? b_base1 : b_base0;
         __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
-                                         (lds_void_t*)(sb + (wave + q * NW) * 1024), 16, 0, 0);
+                                         (lds_void_t*)(sb + (wave + q * NW) * 1024), 16, 0, CP);
       }
     };
 
@@ -408,7 +414,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
     // rows of step ks+1 / the weights of step ks+2.  In the main loop they
     // are compile-time true, so the compiler knows exactly which DMA is still
     // in flight and adds no wait of its own.
-    auto kstep = [&](auto mbac, auto asc, auto bsc, auto nac, auto nbc, int ks) {
+    auto kstep = [&](auto mbac, auto ntc, auto asc, auto bsc, auto nac, auto nbc, int ks) {
       constexpr int MBA = decltype(mbac)::value;
       constexpr int AS = decltype(asc)::value, BS = decltype(bsc)::value;
       const bool next_a = nac, next_b = nbc;
@@ -435,7 +441,7 @@ grouped_gemm_big_kernel(GemmArgs g) {
                               std::is_same_v<decltype(nbc), std::true_type>;
       if constexpr (!SPREAD) {
         if (next_a) issue_a(std::integral_constant<int, (AS + 1) % 2>{}, ks + 1);
-        if (next_b) issue_b(std::integral_constant<int, (BS + 2) % 3>{}, ks + 2);
+        if (next_b) issue_b(std::integral_constant<int, (BS + 2) % 3>{}, ks + 2, ntc);
       }
       // favour this wave's MFMA issue over the other wave on the SIMD
       __builtin_amdgcn_s_setprio(1);
@@ -453,8 +459,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
           char* sb2 = stage_b(std::integral_constant<int, (BS + 2) % 3>{});
           const size_t off = kofs(B16 ? min(ks + 2, nK - 1) : ks + 2);
           const char* bb = up_half(q) ? b_base1 : b_base0;
+          constexpr int CP = decltype(ntc)::value ? kCpolNT : 0;
           __builtin_amdgcn_global_load_lds((glb_void_t*)(bb + b_off[q] + off),
-                                           (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, 0);
+                                           (lds_void_t*)(sb2 + (wave + q * NW) * 1024), 16, 0, CP);
         }
       };
       auto dma_piece = [&](int kk) {
@@ -618,61 +625,79 @@ grouped_gemm_big_kernel(GemmArgs g) {
     // repeat every 6 steps, and the loop runs while every step in it has both
     // refills to issue (ks + 8 <= nK); K is a multiple of 128, so 2, 4 or 6
     // steps remain for the tail.  Returns the first tail step.
-    auto kloop = [&](auto mbac) {
+    auto kloop = [&](auto mbac, auto ntc) {
       // previous tile's epilogue stores and LDS reads must be done before the
       // stages are refilled and before vmcnt counts only this tile's DMA
       wait_vmcnt<0>();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
       issue_a(I0{}, 0);
-      issue_b(I0{}, 0);
-      issue_b(I1{}, 1);  // nK >= 2
+      issue_b(I0{}, 0, ntc);
+      issue_b(I1{}, 1, ntc);  // nK >= 2
       int ks = 0;
       // 320-row tiles run every step here, the last ones refilling stages
       // that are never read (the refill K-step is clamped to the last one)
       for (; ks + (B16 ? 6 : 8) <= nK; ks += 6) {
-        kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
-        kstep(mbac, I1{}, I1{}, T{}, T{}, ks + 1);
-        kstep(mbac, I0{}, I2{}, T{}, T{}, ks + 2);
-        kstep(mbac, I1{}, I0{}, T{}, T{}, ks + 3);
-        kstep(mbac, I0{}, I1{}, T{}, T{}, ks + 4);
-        kstep(mbac, I1{}, I2{}, T{}, T{}, ks + 5);
+        kstep(mbac, ntc, I0{}, I0{}, T{}, T{}, ks);
+        kstep(mbac, ntc, I1{}, I1{}, T{}, T{}, ks + 1);
+        kstep(mbac, ntc, I0{}, I2{}, T{}, T{}, ks + 2);
+        kstep(mbac, ntc, I1{}, I0{}, T{}, T{}, ks + 3);
+        kstep(mbac, ntc, I0{}, I1{}, T{}, T{}, ks + 4);
+        kstep(mbac, ntc, I1{}, I2{}, T{}, T{}, ks + 5);
       }
       if constexpr (B16) {
         // nK is even: 0, 2 or 4 steps remain
         if (ks + 2 <= nK) {
-          kstep(mbac, I0{}, I0{}, T{}, T{}, ks);
-          kstep(mbac, I1{}, I1{}, T{}, T{}, ks + 1);
+          kstep(mbac, ntc, I0{}, I0{}, T{}, T{}, ks);
+          kstep(mbac, ntc, I1{}, I1{}, T{}, T{}, ks + 1);
         }
         if (ks + 4 <= nK) {
-          kstep(mbac, I0{}, I2{}, T{}, T{}, ks + 2);
-          kstep(mbac, I1{}, I0{}, T{}, T{}, ks + 3);
+          kstep(mbac, ntc, I0{}, I2{}, T{}, T{}, ks + 2);
+          kstep(mbac, ntc, I1{}, I0{}, T{}, T{}, ks + 3);
         }
       }
       return ks;
     };
     // a wave with no rows (mba == 0) still loads and waits with the others;
     // its one block of clamped rows is never stored
-    int ks;
-    if (MB >= 5 && mba >= 5) ks = kloop(std::integral_constant<int, MB >= 5 ? 5 : 4>{});
-    else if (mba >= 4) ks = kloop(std::integral_constant<int, 4>{});
-    else if (mba == 3) ks = kloop(std::integral_constant<int, 3>{});
-    else if (mba == 2) ks = kloop(std::integral_constant<int, 2>{});
-    else ks = kloop(std::integral_constant<int, 1>{});
-    // The last 2, 4 or 6 steps run every block (one copy of the code; blocks
-    // without rows are never stored) with refills decided at run time.
-    if constexpr (!B16) {
-      using M4 = std::integral_constant<int, MB>;
-      kstep(M4{}, I0{}, I0{}, ks + 1 < nK, ks + 2 < nK, ks);
-      kstep(M4{}, I1{}, I1{}, ks + 2 < nK, ks + 3 < nK, ks + 1);
-      if (ks + 4 <= nK) {
-        kstep(M4{}, I0{}, I2{}, ks + 3 < nK, ks + 4 < nK, ks + 2);
-        kstep(M4{}, I1{}, I0{}, ks + 4 < nK, ks + 5 < nK, ks + 3);
+    auto run = [&](auto ntc) {
+      int ks;
+      if (MB >= 5 && mba >= 5) ks = kloop(std::integral_constant<int, MB >= 5 ? 5 : 4>{}, ntc);
+      else if (mba >= 4) ks = kloop(std::integral_constant<int, 4>{}, ntc);
+      else if (mba == 3) ks = kloop(std::integral_constant<int, 3>{}, ntc);
+      else if (mba == 2) ks = kloop(std::integral_constant<int, 2>{}, ntc);
+      else ks = kloop(std::integral_constant<int, 1>{}, ntc);
+      // The last 2, 4 or 6 steps run every block (one copy of the code;
+      // blocks without rows are never stored) with refills decided at run
+      // time.
+      if constexpr (!B16) {
+        using M4 = std::integral_constant<int, MB>;
+        kstep(M4{}, ntc, I0{}, I0{}, ks + 1 < nK, ks + 2 < nK, ks);
+        kstep(M4{}, ntc, I1{}, I1{}, ks + 2 < nK, ks + 3 < nK, ks + 1);
+        if (ks + 4 <= nK) {
+          kstep(M4{}, ntc, I0{}, I2{}, ks + 3 < nK, ks + 4 < nK, ks + 2);
+          kstep(M4{}, ntc, I1{}, I0{}, ks + 4 < nK, ks + 5 < nK, ks + 3);
+        }
+        if (ks + 6 <= nK) {
+          kstep(M4{}, ntc, I0{}, I1{}, ks + 5 < nK, ks + 6 < nK, ks + 4);
+          kstep(M4{}, ntc, I1{}, I2{}, false, false, ks + 5);
+        }
       }
-      if (ks + 6 <= nK) {
-        kstep(M4{}, I0{}, I1{}, ks + 5 < nK, ks + 6 < nK, ks + 4);
-        kstep(M4{}, I1{}, I2{}, false, false, ks + 5);
-      }
+    };
+    // Gate/up weight loads are non-temporal when the expert has one m-tile:
+    // no other tile reads its weight slice, which then need not displace
+    // cached token rows (prefill step 11.00 -> 10.87 ms, gate/up 6.76 ->
+    // 6.65 ms; non-temporal loads for every tile had made the small and
+    // skewed batches, whose experts' m-tiles share the slice, 1-3% slower;
+    // for down they gained nothing)
+    using NT0 = std::false_type;
+    using NT1 = std::true_type;
+    if constexpr (MODE == 1 && SHAPE == 1) run(NT1{});
+    else if constexpr (MODE == 1) {
+      if (mt_g == 1) run(NT1{});
+      else run(NT0{});
+    } else {
+      run(NT0{});
     }
 
     // ---- epilogue.  Weights were the MFMA row operand, so block (i, j) is
