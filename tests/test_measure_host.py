@@ -80,3 +80,39 @@ def test_rocpd_stats_skip_and_call_range(tmp_path):
     out = buf.getvalue()
     assert _avg(out, "kernA") == 2.5  # calls 1..2: 2, 3 us
     assert "kernB" not in out
+
+
+def _counter_csv(path, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for i, (name, counter, value) in enumerate(rows):
+            f.write(f'{i},"{name}",{counter},{value}\n')
+
+
+def test_traffic_summary_sums_the_kernels_of_one_call(tmp_path):
+    # one call launches two kernels (320-row and 256-row tiles): the figure
+    # per call is the sum of the two kernels' per-dispatch medians, scaled by
+    # the copy probe's counter KiB per KiB moved
+    a, b = "void grouped_gemm_big_kernel<1, 4, 1>(GemmArgs)", "void grouped_gemm_big_kernel<1, 4, 0>(GemmArgs)"
+    kf, kw = str(tmp_path / "kf.csv"), str(tmp_path / "kw.csv")
+    cf, cw = str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv")
+    _counter_csv(kf, [(a, "FETCH_SIZE", 100.0), (b, "FETCH_SIZE", 50.0), (a, "FETCH_SIZE", 300.0),
+                      (b, "FETCH_SIZE", 70.0), (a, "FETCH_SIZE", 200.0), (b, "FETCH_SIZE", 60.0)])
+    _counter_csv(kw, [(a, "WRITE_SIZE", 10.0), (b, "WRITE_SIZE", 20.0)])
+    kib = TR.COPY_BYTES / 1024.0
+    _counter_csv(cf, [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 0.5 * kib)])
+    _counter_csv(cw, [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1.0 * kib)])
+    src = tmp_path / "k.hip"
+    src.write_text("int k;\n")
+    out = str(tmp_path / "t.txt")
+    args = ["summarize", out, "--kernel-fetch", kf, "--kernel-write", kw, "--copy-fetch", cf,
+            "--copy-write", cw, "--kernel-regex", "grouped_gemm_big_kernel<1,",
+            "--copy-regex", "copyBuffer", "--source", str(src), "--command", "test"]
+    with contextlib.redirect_stdout(io.StringIO()):
+        TR.main(args)
+    s = TR.read_summary(out)
+    # medians 200 + 60 KiB fetched at 0.5 counter KiB per KiB -> 520 KiB read
+    assert float(s["traffic_fetch_bytes"]) == (200.0 + 60.0) * 1024 / 0.5
+    assert float(s["traffic_write_bytes"]) == (10.0 + 20.0) * 1024
+    assert float(s["traffic_bytes"]) == 520 * 1024 + 30 * 1024
+    assert s["source_hash"] == TR.source_hash([str(src)])
