@@ -165,3 +165,23 @@ def test_320_row_tiles_at_exact_row_counts(d, dff):
     err = row_rel_l2(S.to_numpy64(buf.y_perm[:T]), ref["y_perm"])
     say(f"  T={T}, {n320} experts of 257..320 rows; y_perm row relL2 max {err.max():.3e}")
     assert err.max() <= 1e-2
+
+
+@pytest.mark.parametrize("dtype,d", [
+    ("bf16", 2048),   # 256 chunks of 16 bytes per row: one per thread
+    ("bf16", 4096),   # 512
+    ("bf16", 6144),   # 768
+    ("bf16", 8192),   # 1024
+    ("f32", 4096),    # 1024
+    ("bf16", 1536),   # 192: 256 threads, some idle
+    ("f32", 6400),    # 1600: 256 threads looping over the row
+])
+def test_combine_block_widths(dtype, d):
+    # combine runs one thread per 16-byte chunk of a row for 256, 512, 768
+    # and 1024 chunks and 256 looping threads otherwise; every width is
+    # checked against the oracle like the other layer tests (k = 10 takes
+    # the 16-slot variant; with 6 FFN and 10 identity experts a token's
+    # slots mix both kinds, up to identity only)
+    w = S.Workload("combine_width", T=96, d_model=d, n_ffn=6, n_zero=10, d_ff=64, top_k=10,
+                   dtype=dtype, bias_var=0.5, seed=28)
+    full_parity(w)
