@@ -3,11 +3,7 @@
 // zero-computation experts; data sheet table "Mixture of experts": identity
 // zero experts, routed scaling factor).
 //
-// One block per token, one thread per 16-byte chunk of the row when the row
-// has 256, 512, 768 or 1024 of them (else 256 threads that loop over the
-// row), so all of a token's loads are in flight at once (prefill combine
-// 360 -> 349 us, skewed 104 -> 100 us against 256 threads for every width).
-// Wave 0 reads all of the token's slots at once; the
+// One block per token.  Wave 0 reads all of the token's slots at once; the
 // FFN slots (idx < n_ffn) are gathered from y_perm through inv_perm (every
 // slot's load issued before any is summed) and summed with their gates in
 // slot order;
@@ -20,8 +16,8 @@
 
 namespace moe {
 
-template <typename T, int MAXK, int NT>
-__global__ void __launch_bounds__(NT)
+template <typename T, int MAXK>
+__global__ void __launch_bounds__(256)
 combine_kernel(const T* __restrict__ x, const T* __restrict__ y_perm,
                const int32_t* __restrict__ idx, const float* __restrict__ gate,
                const int32_t* __restrict__ inv_perm, int d, int k, int n_ffn,
@@ -69,7 +65,7 @@ combine_kernel(const T* __restrict__ x, const T* __restrict__ y_perm,
   const int nf = s_nf;
   const float gz = s_gz;
   const size_t xrow = (size_t)t * d;
-  for (int c = threadIdx.x; c < d / CE; c += NT) {
+  for (int c = threadIdx.x; c < d / CE; c += 256) {
     // issue every slot's load before accumulating (in slot order); y_perm,
     // x and y are touched once here, so they bypass the caches' retention
     // (non-temporal: prefill combine 0.40 -> 0.36 ms)
@@ -111,17 +107,9 @@ MOE_CHECK_ACCESSOR(check_word_combine)
 int launch_combine(int dtype, const void* x, const void* y_perm, const int32_t* idx,
                    const float* gate, const int32_t* inv_perm, int T, int d, int k, int n_ffn,
                    void* y, hipStream_t st) {
-  const int chunks = d / (dtype == MOE_BF16 ? 8 : 4);
-#define MOE_COMB_NT(TY, MK, NT)                                                            \
-  hipLaunchKernelGGL((combine_kernel<TY, MK, NT>), dim3(T), dim3(NT), 0, st, (const TY*)x, \
+#define MOE_COMB(TY, MK)                                                                  \
+  hipLaunchKernelGGL((combine_kernel<TY, MK>), dim3(T), dim3(256), 0, st, (const TY*)x,   \
                      (const TY*)y_perm, idx, gate, inv_perm, d, k, n_ffn, (TY*)y)
-#define MOE_COMB(TY, MK)                                \
-  do {                                                  \
-    if (chunks == 512) MOE_COMB_NT(TY, MK, 512);        \
-    else if (chunks == 768) MOE_COMB_NT(TY, MK, 768);   \
-    else if (chunks == 1024) MOE_COMB_NT(TY, MK, 1024); \
-    else MOE_COMB_NT(TY, MK, 256);                      \
-  } while (0)
   if (dtype == MOE_BF16) {
     if (k <= 8) MOE_COMB(__bf16, 8);
     else MOE_COMB(__bf16, 16);
@@ -130,7 +118,6 @@ int launch_combine(int dtype, const void* x, const void* y_perm, const int32_t* 
     else MOE_COMB(float, 16);
   }
 #undef MOE_COMB
-#undef MOE_COMB_NT
   return check_launch();
 }
 

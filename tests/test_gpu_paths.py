@@ -168,20 +168,19 @@ def test_320_row_tiles_at_exact_row_counts(d, dff):
 
 
 @pytest.mark.parametrize("dtype,d", [
-    ("bf16", 2048),   # 256 chunks of 16 bytes per row: one per thread
-    ("bf16", 4096),   # 512
-    ("bf16", 6144),   # 768
-    ("bf16", 8192),   # 1024
+    ("bf16", 2048),   # 256 chunks of 16 bytes per row: one per combine thread
+    ("bf16", 4096),   # 512: two per thread
+    ("bf16", 6144),   # 768: three
+    ("bf16", 8192),   # 1024: four
     ("f32", 4096),    # 1024
-    ("bf16", 1536),   # 192: 256 threads, some idle
-    ("f32", 6400),    # 1600: 256 threads looping over the row
+    ("bf16", 1536),   # 192: some threads idle
+    ("f32", 6400),    # 1600: the last pass partial
 ])
-def test_combine_block_widths(dtype, d):
-    # combine runs one thread per 16-byte chunk of a row for 256, 512, 768
-    # and 1024 chunks and 256 looping threads otherwise; every width is
-    # checked against the oracle like the other layer tests (k = 10 takes
-    # the 16-slot variant; with 6 FFN and 10 identity experts a token's
-    # slots mix both kinds, up to identity only)
+def test_combine_row_widths(dtype, d):
+    # combine's 256 threads walk a token's row in 16-byte chunks; every
+    # width is checked against the oracle like the other layer tests (k = 10
+    # takes the 16-slot variant; with 6 FFN and 10 identity experts a
+    # token's slots mix both kinds, up to identity only)
     w = S.Workload("combine_width", T=96, d_model=d, n_ffn=6, n_zero=10, d_ff=64, top_k=10,
                    dtype=dtype, bias_var=0.5, seed=28)
     full_parity(w)
