@@ -89,7 +89,7 @@ def test_mtile_bound_is_the_brute_force_maximum():
                 if last < 0:
                     continue
                 best = max(best, sum(cdiv(c, 256) for c in list(comb) + [last]))
-            # the driver's bound for this case (T = rows, k = 1)
+            # the host plan's bound for this case (T = rows, k = 1)
             mx = rows if rows <= n_groups else n_groups + (rows - n_groups) // 256
             assert best <= mx, (n_groups, rows, best, mx)
             assert sum(cdiv(c, 256) for c in worst_counts(rows, n_groups)) == mx
