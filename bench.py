@@ -145,6 +145,10 @@ def gate_up_kernel_name(w):
             or Tk // w.n_ffn >= 64)
     if (tall and w.dtype == "bf16" and w.d_model % 128 == 0 and w.d_ff % 128 == 0
             and cdiv(Tk, 256) * min(w.d_ff // 128, w.d_model // 256) >= 64):
+        if w.d_model >= 4096:  # the 256x256 tiles on 16x16x32 MFMAs from d_model 4096
+            return ("grouped_gemm_big_kernel<1,4,1|2> (320x192 tiles for the experts of "
+                    "257..320 rows when they fill 4 rounds of the grid, then 256x256 tiles on "
+                    "16x16x32 MFMAs for the rest; gate/up + SwiGLU; event time of both launches)")
         return ("grouped_gemm_big_kernel<1,4,1|0> (320x192 tiles for the experts of 257..320 "
                 "rows when they fill 4 rounds of the grid, then 256x256 tiles for the rest; "
                 "gate/up + SwiGLU; event time of both launches)")

@@ -79,6 +79,7 @@ __device__ __forceinline__ void wait_lgkm0() {
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
 constexpr int kBigMaxGroups = 1024;
+constexpr int kGateUp16MinK = 4096;  // gate/up's 256 x 256 tiles on 16x16x32 MFMAs from here
 constexpr int kBigDescRegs = 4;  // tile descriptors: 64 per register
 static_assert(64 * kBigDescRegs == plan::kBigMaxTilesPerWg, "host bound on items per workgroup");
 static_assert(kBigMaxGroups == plan::kBigMaxGroups && kBigTileRows == plan::kBigTileRows,
@@ -87,17 +88,17 @@ static_assert(plan::kR320Lo > kBigTileRows && plan::kR320Hi <= 320, "320-row til
 
 // The tile shapes.
 //  0: 256 x 256 on 32x32x16 MFMAs, 8 waves of 128 x 64: the router, and the
-//     gate/up experts outside 257..320 rows.
+//     gate/up experts outside 257..320 rows when d_model < 4096.
 //  1: 320 x 192 on 16x16x32 MFMAs, 8 waves of 80 x 96 (120 accumulators per
 //     lane, 152 KiB of LDS): an expert with 257..320 rows in one tile
 //     instead of two, so its weight slice passes through LDS once.
 //  2: 256 x 256 on 16x16x32 MFMAs, 8 waves of 64 x 128: the down experts
-//     outside 257..320 rows.  Rows come in blocks of 16, so a tile's last
-//     block carries 8 padding rows on average instead of 16, and it ran
-//     faster than shape 0 for down on every workload (prefill 3.83 -> 3.73
-//     ms); for gate/up it was slower on the skewed and small batches.  Its
-//     fragments are read once per K-slice (a second set does not fit next
-//     to 128 accumulators).
+//     outside 257..320 rows, and the gate/up ones when d_model >= 4096.
+//     Rows come in blocks of 16, so a tile's last block carries 8 padding
+//     rows on average instead of 16; it ran faster than shape 0 for down on
+//     every workload (prefill 3.83 -> 3.73 ms).  Its fragments are read
+//     once per K-slice (a second set does not fit next to 128
+//     accumulators).
 template <int SHAPE>
 struct BigShape {
   static constexpr int BM = SHAPE == 1 ? 320 : 256, BN = SHAPE == 1 ? 192 : 256;
@@ -821,14 +822,19 @@ static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
 
 // Expert modes: the groups of r320_lo..r320_hi rows on 320 x 192 tiles, the
 // others on 256 x 256 tiles (two launches on the same stream; they write
-// disjoint rows).
+// disjoint rows).  Down's 256 x 256 tiles always run on 16x16x32 MFMAs;
+// gate/up's do when d_model (its K) is at least kGateUp16MinK: then the
+// whole layer step was faster (prefill 10.73-10.85 -> 10.63 ms, skewed
+// 1.69 -> 1.65 ms: gate/up about even, the down GEMM after it 2-4% faster),
+// with d_model 2048 slower (small 0.41 -> 0.42 ms).
 template <int MODE>
 static int launch_big_expert(const GemmArgs& g, hipStream_t st) {
   if (g.r320_hi > 0) {
     const int rc = launch_big_mode<MODE, 1>(g, st);
     if (rc != MOE_OK) return rc;
   }
-  return launch_big_mode<MODE, MODE == 2 ? 2 : 0>(g, st);
+  if (MODE == 2 || g.K >= kGateUp16MinK) return launch_big_mode<MODE, 2>(g, st);
+  return launch_big_mode<MODE, 0>(g, st);
 }
 
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
