@@ -157,13 +157,13 @@ def gate_up_kernel_name(w):
     return "grouped_gemm_kernel mode 1 (16x256 tiles, gate/up + SwiGLU)"
 
 
-def measured_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter summary of
-    this workload, or None when there is none or the GEMM sources changed
-    since the counters were taken."""
+def measured_traffic(workload, kernel="gate_up"):
+    """HBM bytes per gate/up (or down) launch from the committed counter
+    summary of this workload, or None when there is none or the GEMM
+    sources changed since the counters were taken."""
     from sparse_moe_layer_03_amd import traffic as TR
 
-    summ = TR.read_summary(os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.txt"))
+    summ = TR.read_summary(os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt"))
     if not summ:
         return None
     srcs = [os.path.join(ROOT, p) for p in summ.get("sources", [])]
@@ -656,6 +656,7 @@ def run_workload(w, args, mdl, dev, cpu=True):
     by_d = [el * (1.0 * u * w.d_model * w.d_ff + a * w.d_ff + a * w.d_model)
             for a, u in zip(A, U)]
     roof_d = kernel_roofline(down_kernel_name(w), fl_d, by_d, dn_ms / 1e3, peak_fl)
+    roof_d["traffic"] = measured_traffic(w.name, "down")
 
     # whole-layer figures per step from its exact A (FFN assignments) and U
     # (touched FFN experts): F = 2 T d E + 6 A d d_ff flops; B_min = the

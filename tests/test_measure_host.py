@@ -36,13 +36,27 @@ def test_source_hash_depends_on_file_names_not_argument_order(tmp_path):
 
 
 def test_committed_traffic_summaries_parse():
-    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_gate_up_*.txt")))
-    assert paths
+    paths = sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.txt")))
+    assert any("traffic_gate_up_" in p for p in paths)
+    assert any("traffic_down_" in p for p in paths)
     for p in paths:
         s = TR.read_summary(p)
         assert re.fullmatch(r"[0-9a-f]{16}", s["source_hash"]), p
         assert float(s["traffic_bytes"]) > 0, p
         assert s["sources"] and all(os.path.exists(os.path.join(ROOT, q)) for q in s["sources"]), p
+
+
+def test_bench_traffic_follows_the_summary_and_its_source_hash():
+    import bench
+
+    for kernel in ("gate_up", "down"):
+        for p in sorted(glob.glob(os.path.join(ROOT, "profiles", f"traffic_{kernel}_*.txt"))):
+            w = os.path.basename(p)[len(f"traffic_{kernel}_"):-len(".txt")]
+            s = TR.read_summary(p)
+            fresh = TR.source_hash([os.path.join(ROOT, q) for q in s["sources"]]) == s["source_hash"]
+            got = bench.measured_traffic(w, kernel)
+            assert got == (float(s["traffic_bytes"]) if fresh else None), p
+    assert bench.measured_traffic("no_such_workload", "down") is None
 
 
 def _db(path, durations):
