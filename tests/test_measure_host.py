@@ -130,3 +130,13 @@ def test_traffic_summary_sums_the_kernels_of_one_call(tmp_path):
     assert float(s["traffic_write_bytes"]) == (10.0 + 20.0) * 1024
     assert float(s["traffic_bytes"]) == 520 * 1024 + 30 * 1024
     assert s["source_hash"] == TR.source_hash([str(src)])
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2 and r.stdout == ""
+    assert "one GPU only" in r.stderr
