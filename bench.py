@@ -105,6 +105,10 @@ def parse():
                          "router matrix is read on a second stream while a layer's expert "
                          "GEMMs run (Infinity Cache warm-up)")
     ap.add_argument("--prefetch", action="store_true")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the named workload's model and value distributions at this many "
+                         "tokens per batch instead (a batch-size sweep; the config is named "
+                         "<workload>@T<tokens>); not for the default headline run")
     ap.add_argument("--balance", type=float, default=0.0,
                     help="per-expert load-balancing step (moe_balance_update) after the PID; "
                          "0 = off")
@@ -859,6 +863,11 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the layer is measured on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+    if args.tokens and (args.tokens < 1 or args.workload == "headline" or args.scmoe
+                        or args.layers):
+        print("bench.py: --tokens takes a positive count and a --workload other than the "
+              "default headline run (no --scmoe / --layers)", file=sys.stderr)
+        sys.exit(2)
     if args.scmoe:
         if args.workload == "headline":
             args.workload = "decode_bf16"
@@ -876,6 +885,10 @@ def main():
     dev = "cuda"
     if args.workload != "headline":
         w = S.WORKLOADS[args.workload]
+        if args.tokens:
+            import dataclasses
+
+            w = dataclasses.replace(w, T=args.tokens, name=f"{w.name}@T{args.tokens}")
         line = run_workload(w, args, build_model(w, dev), dev)
         print(json.dumps(line), flush=True)
         return

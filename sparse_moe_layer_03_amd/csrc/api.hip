@@ -252,9 +252,13 @@ int moe_dispatch(const moe_shape* s, const int32_t* topk_idx, const void* x, int
                       (hipStream_t)stream);
 }
 
-// Experts of 257..320 rows on the 320 x 192 tiles, where the shape allows.
-static void set_r320(const moe_shape* s, GemmArgs& g, hipStream_t st) {
-  if (plan::ffn_use_r320(s->T, s->top_k, s->n_ffn, s->d_model, s->d_ff, big_grid(st))) {
+// Many-row launch settings: the grid multiple that keeps every workgroup
+// within its descriptor registers, and the experts of 257..320 rows on the
+// 320 x 192 tiles where the shape allows.
+static void set_big(const moe_shape* s, GemmArgs& g, hipStream_t st) {
+  const int G = big_grid(st);
+  g.grid_mult = (int)plan::big_grid_mult(s->T, s->top_k, s->n_ffn, s->d_model, s->d_ff, G);
+  if (plan::ffn_use_r320(s->T, s->top_k, s->n_ffn, s->d_model, s->d_ff, G)) {
     g.r320_lo = plan::kR320Lo;
     g.r320_hi = plan::kR320Hi;
   }
@@ -283,7 +287,7 @@ int moe_ffn_gate_up(const moe_shape* s, const void* x, const void* x_perm, const
   g.top_k = s->top_k;
   g.ksplit = 1;
   if (ffn_use_big(s, x_perm == nullptr, (hipStream_t)stream)) {
-    set_r320(s, g, (hipStream_t)stream);
+    set_big(s, g, (hipStream_t)stream);
     return launch_gemm_big(1, g, (hipStream_t)stream);
   }
   return launch_gemm(s->dtype, 1, ffn_big_tiles(s), g, (hipStream_t)stream);
@@ -307,7 +311,7 @@ int moe_ffn_down(const moe_shape* s, const int32_t* offsets, const void* w_down,
   g.M = s->T;
   g.ksplit = 1;
   if (ffn_use_big(s, false, (hipStream_t)stream)) {
-    set_r320(s, g, (hipStream_t)stream);
+    set_big(s, g, (hipStream_t)stream);
     return launch_gemm_big(2, g, (hipStream_t)stream);
   }
   return launch_gemm(s->dtype, 2, ffn_big_tiles(s), g, (hipStream_t)stream);

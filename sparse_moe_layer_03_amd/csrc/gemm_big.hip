@@ -182,7 +182,9 @@ grouped_gemm_big_kernel(GemmArgs g) {
     if (tid == NT - 1) s_scan[NT / 64] = incl;
     __syncthreads();
     constexpr int HN320 = MODE == 1 ? BigShape<true>::BN / 2 : BigShape<true>::BN;
-    use320 = s_scan[NT / 64] * ((g.N + HN320 - 1) / HN320) >= 4 * (int)gridDim.x;
+    // (four rounds of one workgroup per CU: the grid is grid_mult of them)
+    use320 = s_scan[NT / 64] * ((g.N + HN320 - 1) / HN320) >=
+             4 * (int)gridDim.x / max(1, g.grid_mult);
   }
   // m-tiles of a group of cnt rows on this kernel (none for the groups the
   // other tile shape runs)
@@ -816,7 +818,9 @@ template <int MODE, int SHAPE>
 static int launch_big_mode(const GemmArgs& g, hipStream_t st) {
   auto kern = grouped_gemm_big_kernel<MODE, MOE_BIG_MG, SHAPE>;
   if (device_cu_count() <= 0) return MOE_EHIP;
-  hipLaunchKernelGGL(kern, dim3(big_grid(st)), dim3(512), 0, st, g);
+  // expert modes: grid_mult waves of one workgroup per CU (plan::big_grid_mult)
+  const int mult = (MODE != 0 && g.grid_mult > 1) ? g.grid_mult : 1;
+  hipLaunchKernelGGL(kern, dim3(big_grid(st) * mult), dim3(512), 0, st, g);
   return check_launch();
 }
 
@@ -845,6 +849,7 @@ int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st) {
     return launch_big_mode<0, 0>(g, st);
   }
   if (g.r320_hi > 0 && (g.r320_lo < 1 || g.r320_hi > 320)) return MOE_EINVAL;
+  if (g.grid_mult < 0 || g.grid_mult > plan::kBigMaxGridMult) return MOE_EINVAL;
   return mode == 1 ? launch_big_expert<1>(g, st) : launch_big_expert<2>(g, st);
 }
 

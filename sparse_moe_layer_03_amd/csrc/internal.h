@@ -24,6 +24,9 @@ struct GemmArgs {
   int ksplit;              // router: K is split into this many partial sums
   int r320_lo, r320_hi;    // many-row expert modes: groups of r320_lo..r320_hi
                            // rows run on 320 x 192 tiles (r320_hi 0: none)
+  int grid_mult;           // many-row expert modes: launch big_grid() times this
+                           // many workgroups (plan::big_grid_mult; 0 or 1: one
+                           // per CU)
 };
 
 // mode: 0 router, 1 gate/up + SwiGLU, 2 down.  big: 128x128 tiles, else
@@ -33,8 +36,8 @@ int launch_gemm(int dtype, int mode, int big, const GemmArgs& g, hipStream_t st)
 // bf16 gate/up (mode 1) or down (mode 2) with 256x256 direct-to-LDS tiles,
 // and 320x192 tiles for the groups of r320_lo..r320_hi rows (K a multiple of
 // 128, at most 1024 groups, at most 256 tiles per workgroup of the
-// big_grid() launched: plan::ffn_use_big, plan::ffn_use_r320); mode 0: the
-// router GEMM.
+// big_grid() * grid_mult launched: plan::ffn_use_big, plan::big_grid_mult,
+// plan::ffn_use_r320); mode 0: the router GEMM.
 constexpr int kBigTileRows = 256;
 int launch_gemm_big(int mode, const GemmArgs& g, hipStream_t st);
 // Workgroups of a many-row launch on stream st (one per CU it may use).

@@ -64,9 +64,25 @@ inline bool ffn_tall_tiles(long T, long top_k, long n_ffn, long n_zero, long d_m
          Tk / n_ffn >= 64;
 }
 
+// Workgroups of a many-row launch are G (one per CU) times the smallest
+// multiple m that keeps every workgroup within kBigMaxTilesPerWg items for
+// the worst spread of rows over experts, in both modes.  One workgroup fills
+// a CU's LDS, so a grid of G * m runs as m waves of persistent workgroups
+// (same work, same tile order within an XCD); the kernel takes its grid size
+// from the launch.  Returns 0 when no m up to kBigMaxGridMult does.
+constexpr long kBigMaxGridMult = 64;
+inline long big_grid_mult(long T, long top_k, long n_ffn, long d_model, long d_ff, long G) {
+  if (G < 1) return 0;
+  const long mt = big_mtiles_max(T * top_k, n_ffn);
+  const long nt = std::max(big_ntiles(1, d_model, d_ff), big_ntiles(2, d_model, d_ff));
+  for (long m = 1; m <= kBigMaxGridMult; ++m)
+    if (big_items_per_wg_max(mt * nt, G * m) <= kBigMaxTilesPerWg) return m;
+  return 0;
+}
+
 // Whether the expert GEMMs of a bf16 shape run on the many-row kernel
 // (256x256 direct-to-LDS tiles, with 320x192 ones beside them:
-// ffn_use_r320), for a grid of G workgroups.  `gather`:
+// ffn_use_r320), for G workgroups per wave (big_grid_mult waves).  `gather`:
 // gate/up reads x rows through perm (token rows anywhere in x, addressed by
 // 32-bit offsets from x, so x must stay below 4 GiB); otherwise token rows
 // (x_perm or H) are contiguous per tile and addressed from a 64-bit tile
@@ -82,17 +98,18 @@ inline bool ffn_use_big(long T, long top_k, long n_ffn, long n_zero, long d_mode
   // enough tiles to spread over the chip
   const long nt_min = std::min(big_ntiles(1, d_model, d_ff), big_ntiles(2, d_model, d_ff));
   if (cdiv(Tk, kBigTileRows) * nt_min < kMinTiles) return false;
-  // every workgroup tracks at most 256 items, in both modes
-  const long mt = big_mtiles_max(Tk, n_ffn);
-  if (mt >= kBigMaxMTiles) return false;
-  const long nt = std::max(big_ntiles(1, d_model, d_ff), big_ntiles(2, d_model, d_ff));
-  return big_items_per_wg_max(mt * nt, G) <= kBigMaxTilesPerWg;
+  // every workgroup tracks at most 256 items, in both modes, on a grid of
+  // G * big_grid_mult workgroups
+  if (big_mtiles_max(Tk, n_ffn) >= kBigMaxMTiles) return false;
+  return big_grid_mult(T, top_k, n_ffn, d_model, d_ff, G) > 0;
 }
 
 // Whether a many-row shape also uses the 320-row tiles: at most
 // min(n_ffn, T*k / 257) groups take one such tile each, and every workgroup
-// tracks at most 256 items of that launch too, in both modes.  (The kernel
-// uses them only when the groups in range fill four rounds of the grid.)
+// tracks at most 256 items of that launch too, in both modes, on G
+// workgroups (the launch runs on the same G * big_grid_mult grid as the
+// 256-row one, which only lowers that count).  (The kernel uses them only
+// when the groups in range fill four rounds of the grid.)
 inline bool ffn_use_r320(long T, long top_k, long n_ffn, long d_model, long d_ff, long G) {
   const long groups = std::min(n_ffn, T * top_k / kR320Lo);
   if (groups < 1 || G < 1) return false;

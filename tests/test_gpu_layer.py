@@ -138,3 +138,18 @@ def test_prefill_model_twice_the_batch(big_model, n_min):
     toks, tiles, _ = covering_tokens(gpu, w.n_ffn, w.top_k, n_min, seed=13)
     say(f"  {len(tiles)} m-tiles, every one hit by a sampled token")
     check_sampled_outputs(big_model, x, gpu, toks, tol, "prefill model, T=32768")
+
+
+@pytest.mark.parametrize("n_min", [1024])
+def test_prefill_model_four_times_the_batch(big_model, n_min):
+    # 65536 tokens: 786,432 assignments, about 1024 rows per expert.  For the
+    # worst spread of rows the descriptor registers of a one-per-CU grid
+    # would not hold every workgroup's tiles, so the many-row kernel runs on
+    # twice the CU count of workgroups, in two waves (plan::big_grid_mult)
+    w = S.Workload("prefill64k_bf16", T=65536, d_model=6144, n_ffn=512, n_zero=256, d_ff=2048,
+                   top_k=12, dtype="bf16")
+    say(f"[parity] {w}")
+    x, gpu, tol = _run_big(big_model, w)
+    toks, tiles, _ = covering_tokens(gpu, w.n_ffn, w.top_k, n_min, seed=17)
+    say(f"  {len(tiles)} m-tiles, every one hit by a sampled token")
+    check_sampled_outputs(big_model, x, gpu, toks, tol, "prefill model, T=65536")

@@ -1,7 +1,8 @@
 """Host-only check of the expert-GEMM launch plan (csrc/plan.h): whenever a
 shape is sent to the many-row kernel, no workgroup of its persistent grid
-gets more work items than the four descriptor registers it keeps (256), in
-either mode, for the worst-case spread of rows over experts.
+(G workgroups per wave, big_grid_mult waves) gets more work items than the
+four descriptor registers it keeps (256), in either mode, for the
+worst-case spread of rows over experts.
 
 The plan header is plain C++; a tiny driver built with g++ prints its
 decisions.  The item count of the kernel is recomputed here from the
@@ -27,8 +28,9 @@ int main() {
   long T, k, N, Z, d, dff, bf16, gather, G;
   while (scanf("%ld %ld %ld %ld %ld %ld %ld %ld %ld", &T, &k, &N, &Z, &d, &dff, &bf16,
                &gather, &G) == 9) {
-    printf("%d %ld %d\n", (int)moe::plan::ffn_use_big(T, k, N, Z, d, dff, bf16 != 0, gather != 0, G),
-           moe::plan::big_mtiles_max(T * k, N), (int)moe::plan::ffn_use_r320(T, k, N, d, dff, G));
+    printf("%d %ld %d %ld\n", (int)moe::plan::ffn_use_big(T, k, N, Z, d, dff, bf16 != 0, gather != 0, G),
+           moe::plan::big_mtiles_max(T * k, N), (int)moe::plan::ffn_use_r320(T, k, N, d, dff, G),
+           moe::plan::big_grid_mult(T, k, N, d, dff, G));
   }
   return 0;
 }
@@ -99,6 +101,7 @@ SHAPES = [
     # T, k, N, Z, d_model, d_ff
     (16384, 12, 512, 256, 6144, 2048),    # prefill
     (32768, 12, 512, 256, 6144, 2048),    # twice the prefill batch
+    (65536, 12, 512, 256, 6144, 2048),    # four times: two waves of workgroups
     (8192, 8, 256, 128, 4096, 1536),      # skewed
     (4096, 8, 64, 32, 2048, 1024),        # small
     (2048, 4, 16, 8, 512, 384),
@@ -117,17 +120,20 @@ def test_many_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
     res = plan_driver(rows)
     rng = np.random.default_rng(G)
     n_big, most = 0, 0
-    for (T, k, N, Z, d, dff), (big, mt_max, _) in zip(SHAPES, res):
+    for (T, k, N, Z, d, dff), (big, mt_max, _, mult) in zip(SHAPES, res):
         if not big:
             continue
         n_big += 1
+        assert 1 <= mult <= 64
+        if mult > 1:   # the smallest multiple: one wave fewer would not fit
+            assert cdiv(mt_max * max(cdiv(dff, 128), cdiv(d, 256)), G * (mult - 1)) > 256
         Tk = T * k
         dists = [worst_counts(Tk, N), rng.multinomial(Tk, np.full(N, 1.0 / N)),
                  rng.multinomial(Tk, rng.dirichlet(np.full(N, 0.3)))]
         for counts in dists:
             assert sum(cdiv(int(c), 256) for c in counts) <= mt_max
             for ntiles in (cdiv(dff, 128), cdiv(d, 256)):     # gate/up, down
-                items = kernel_items_per_wg(counts, ntiles, G)
+                items = kernel_items_per_wg(counts, ntiles, G * mult)
                 most = max(most, items)
                 assert items <= 256, (T, k, N, d, dff, G)
     if G == 256:
@@ -144,13 +150,19 @@ def test_plan_refuses_shapes_past_the_limits(plan_driver):
         (400_000, 12, 512, 256, 6144, 2048, 1, 0, 256),  # same rows contiguous: tile count decides
         (6_000_000 // 8, 8, 64, 0, 640, 256, 1, 1, 256),
         (32768, 12, 512, 256, 6144, 2048, 1, 1, 256),   # twice the prefill batch: yes
+        (65536, 12, 512, 256, 6144, 2048, 1, 1, 256),   # four times: yes, two waves
+        (1_000_000, 16, 1024, 0, 128, 4096, 1, 1, 8),   # 8 CUs: more than 64 waves needed
     ])
     assert res[0][0] == 0 and res[1][0] == 1 and res[2][0] == 0
+    assert res[1][3] == 1 and res[5][3] == 1
     # 6M assignments at d_model 640: the down GEMM's 3 n-tiles per m-tile
-    # would give a workgroup more than 256 items
+    # would give a workgroup of a one-wave grid more than 256 items; two
+    # waves of workgroups hold them
     mt = res[4][1]
-    assert cdiv(mt * 3, 256) > 256 and res[4][0] == 0
+    assert cdiv(mt * 3, 256) > 256 and res[4][0] == 1 and res[4][3] == 2
     assert res[5][0] == 1
+    assert res[6][0] == 1 and res[6][3] == 2
+    assert res[7][0] == 0 and res[7][3] == 0
 
 
 def counts_320(Tk, N, rng):
@@ -167,12 +179,12 @@ def test_320_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
     """When a shape also uses the 320 x 192 tiles (experts of 257..320 rows),
     that launch's work items per workgroup stay within the 256 descriptor
     slots in both modes, and the 256-row launch's (which skips those
-    experts) too."""
+    experts) too, on the grid both launches share."""
     rows = [(T, k, N, Z, d, dff, 1, 1, G) for (T, k, N, Z, d, dff) in SHAPES]
     res = plan_driver(rows)
     rng = np.random.default_rng(7 + G)
     used = 0
-    for (T, k, N, Z, d, dff), (big, _, r320) in zip(SHAPES, res):
+    for (T, k, N, Z, d, dff), (big, _, r320, mult) in zip(SHAPES, res):
         if not (big and r320):
             continue
         used += 1
@@ -180,7 +192,8 @@ def test_320_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
             tall = [int(c) for c in counts if 257 <= c <= 320]
             rest = [int(c) for c in counts if not 257 <= c <= 320]
             for nt320, nt256 in ((cdiv(dff, 96), cdiv(dff, 128)), (cdiv(d, 192), cdiv(d, 256))):
-                assert kernel_items_per_wg(tall, nt320, G, rows=320) <= 256
-                assert kernel_items_per_wg(rest, nt256, G) <= 256
+                # both launches run on the same grid of G * mult workgroups
+                assert kernel_items_per_wg(tall, nt320, G * mult, rows=320) <= 256
+                assert kernel_items_per_wg(rest, nt256, G * mult) <= 256
     if G == 256:
         assert used >= 3, used
