@@ -133,16 +133,24 @@ def test_moe_and_dense_on_cu_partitioned_streams_match_serial(dense_cus, pattern
         ds.close()
 
 
-@pytest.mark.parametrize("cus", [64, 32])
-def test_many_row_gemms_on_a_cu_masked_stream_match_the_full_chip(cus):
+@pytest.mark.parametrize("cus,T,N", [(64, 3480, 48), (32, 3480, 48), (32, 14500, 200)])
+def test_many_row_gemms_on_a_cu_masked_stream_match_the_full_chip(cus, T, N):
     # The whole layer on a stream restricted to `cus` contiguous CUs: the
-    # persistent expert GEMMs (256x256 and 320x192 tiles; 38 of 48 experts
-    # hold 257..320 rows) size their grids by the stream's CU mask, so the
-    # tiles land on other workgroups and the last round is cut differently,
-    # and the outputs still equal the full-chip run bit for bit.
-    w = S.Workload("rows320", T=3480, d_model=512, n_ffn=48, n_zero=0, d_ff=4096, top_k=4,
+    # persistent expert GEMMs (256x256 and 320x192 tiles; most experts hold
+    # 257..320 rows) size their grids by the stream's CU mask, so the tiles
+    # land on other workgroups and the last round is cut differently, and
+    # the outputs still equal the full-chip run bit for bit.  With 200
+    # experts on 32 CUs the worst-case tile count needs two waves of
+    # workgroups (the plan's grid multiple), the full chip one.
+    w = S.Workload("rows320", T=T, d_model=512, n_ffn=N, n_zero=0, d_ff=4096, top_k=4,
                    dtype="bf16", bias_var=0.0, seed=27)
-    say(f"layer on a {cus}-CU stream vs the full chip")
+    cdiv = lambda a, b: -(-a // b)  # noqa: E731
+    Tk = T * w.top_k
+    tiles_max = (N + (Tk - N) // 256) * max(cdiv(w.d_ff, 128), cdiv(w.d_model, 256))
+    waves = 1 if cdiv(tiles_max, cus) <= 256 else 2
+    assert cdiv(tiles_max, cus * waves) <= 256
+    assert waves == (2 if N == 200 else 1)
+    say(f"layer on a {cus}-CU stream ({waves} wave(s) of workgroups) vs the full chip")
     m = Model(w)
     x = S.make_x(w, 0, "cuda")
     buf = B.LayerBuffers(m.shape, "cuda")
