@@ -197,3 +197,39 @@ def test_320_row_kernel_items_fit_the_descriptor_registers(plan_driver, G):
                 assert kernel_items_per_wg(rest, nt256, G * mult) <= 256
     if G == 256:
         assert used >= 3, used
+
+
+def test_grid_multiple_over_random_shapes(plan_driver):
+    """Seeded random shapes and CU counts: whenever the plan takes the
+    many-row kernel, the worst-case and sampled row spreads keep every
+    workgroup of the G * mult grid within 256 items in both modes, and one
+    wave fewer would not."""
+    rng = np.random.default_rng(2024)
+    rows, shapes = [], []
+    for _ in range(300):
+        N = int(rng.choice([8, 64, 256, 512, 1000, 1024]))
+        Z = int(rng.integers(0, 1025 - N))
+        k = int(rng.integers(1, min(16, N + Z) + 1))
+        d = 128 * int(rng.integers(1, 65))
+        dff = 128 * int(rng.integers(1, 65))
+        T = int(rng.integers(1, min(2 ** 31 // k - 1, 3_000_000)))
+        G = int(rng.choice([8, 32, 64, 248, 256]))
+        rows.append((T, k, N, Z, d, dff, 1, 0, G))
+        shapes.append((T, k, N, Z, d, dff, G))
+    res = plan_driver(rows)
+    n_big = n_mult = 0
+    for (T, k, N, Z, d, dff, G), (big, mt_max, _, mult) in zip(shapes, res):
+        if not big:
+            continue
+        n_big += 1
+        n_mult += mult > 1
+        assert 1 <= mult <= 64
+        nt = max(cdiv(dff, 128), cdiv(d, 256))
+        assert cdiv(mt_max * nt, G * mult) <= 256
+        if mult > 1:
+            assert cdiv(mt_max * nt, G * (mult - 1)) > 256
+        Tk = T * k
+        for counts in (worst_counts(Tk, N), rng.multinomial(Tk, np.full(N, 1.0 / N))):
+            for ntiles in (cdiv(dff, 128), cdiv(d, 256)):
+                assert kernel_items_per_wg(counts, ntiles, G * mult) <= 256, (T, k, N, d, dff, G)
+    assert n_big >= 50 and n_mult >= 10, (n_big, n_mult)
